@@ -1,0 +1,418 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each pin takes an `Oracle` (possibly a deliberately broken build of it, see
+test_oracle_mutants.py) and raises AssertionError when the oracle disagrees
+with the fact.  The facts come from the pages (a hand-worked instance of the
+four-step walk-through, renormalised weights summing to one, unselected
+experts contributing nothing, the average of T*K/E rows per expert, the
+capacity cut, the aux-loss formula, the bias sign rule), from mathematics
+(closed forms, brute force over all subsets, O(n^2) ranks) and from library
+routines (numpy float64 matmul).
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------
+
+def pin_walkthrough_golden(orc):
+    """Hand-built instance of the four-step walk-through (cf-1.com notes §2)."""
+    g = _golden("walkthrough_t1_e4_k2.json")
+    logits = np.array(g["logits"], np.float32)
+    ids, w, probs = orc.route(logits, g["K"])
+    assert ids.tolist() == g["expect_ids"], ids
+    np.testing.assert_allclose(w, np.array(g["expect_w"]), rtol=0, atol=1e-15)
+    x = np.array(g["x"], np.float32)
+    w1 = np.array(g["w1"], np.float32)
+    w3 = np.array(g["w3"], np.float32)
+    w2 = np.array(g["w2"], np.float32)
+    h0 = orc.expert(x[0], w1[0], w3[0], w2[0])
+    h1 = orc.expert(x[0], w1[1], w3[1], w2[1])
+    np.testing.assert_allclose(h0, g["expect_h0"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(h1, g["expect_h1"], rtol=0, atol=1e-14)
+    y = orc.layer_output(x, w1, w3, w2, ids, w)
+    np.testing.assert_allclose(y, np.array(g["expect_y"]), rtol=0, atol=1e-14)
+
+
+def pin_softmax_and_renorm_sum_to_one(orc):
+    """Softmax over all E sums to 1; renormalised top-K weights sum to 1 (notes §2.1)."""
+    r = _rng(1)
+    for E, K in ((8, 2), (64, 2), (256, 8), (5, 5)):
+        logits = (r.standard_normal((37, E)) * 3).astype(np.float32)
+        ids, w, probs = orc.route(logits, K)
+        np.testing.assert_allclose(probs.sum(1), 1.0, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=1e-14)
+        assert (w > 0).all()
+
+
+def _numpy_topk_then_softmax(logits, bias, K):
+    """The engineering page's router (§1): top-K on the logits, then a softmax
+    over the K chosen logits.  Stable order: value descending, index ascending."""
+    lp = logits.astype(np.float32) + (np.float32(0) if bias is None else bias.astype(np.float32))
+    lp = lp.astype(np.float32)
+    T, E = lp.shape
+    ids = np.empty((T, K), np.int64)
+    w = np.empty((T, K), np.float64)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -lp[t].astype(np.float64)))
+        sel = order[:K]
+        ids[t] = sel
+        v = lp[t, sel].astype(np.float64)
+        ev = np.exp(v - v.max())
+        w[t] = ev / ev.sum()
+    return ids, w
+
+
+def pin_two_router_formulations_agree(orc):
+    """Notes §2 (softmax over all, top-K, renormalise) equals the engineering page
+    §1 (top-K on logits, softmax over those K), with and without a bias (§1.2)."""
+    r = _rng(2)
+    for E, K, with_bias in ((8, 2, False), (8, 2, True), (64, 2, True), (256, 8, True), (16, 1, False)):
+        logits = (r.standard_normal((41, E)) * 2).astype(np.float32)
+        bias = (r.uniform(-1, 1, E)).astype(np.float32) if with_bias else None
+        ids, w, _ = orc.route(logits, K, bias)
+        ids_n, w_n = _numpy_topk_then_softmax(logits, bias, K)
+        assert np.array_equal(ids, ids_n)
+        np.testing.assert_allclose(w, w_n, rtol=0, atol=1e-12)
+
+
+def pin_topk_bruteforce_ties(orc):
+    """Brute force over all C(E,K) subsets on tie-heavy logits (incl. -0.0 vs +0.0):
+    the chosen set has the maximal sum and is the lexicographically smallest such
+    set; the order within it is value descending, index ascending."""
+    r = _rng(3)
+    for E in (2, 3, 5, 8):
+        for K in range(1, E + 1):
+            vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0], np.float32)
+            logits = r.choice(vals, size=(25, E)).astype(np.float32)
+            ids, _, _ = orc.route(logits, K)
+            for t in range(logits.shape[0]):
+                lt = logits[t].astype(np.float64)
+                best = None
+                for sub in itertools.combinations(range(E), K):
+                    s = sum(lt[list(sub)])
+                    if best is None or s > best[0] or (s == best[0] and sub < best[1]):
+                        best = (s, sub)
+                expect = sorted(best[1], key=lambda e: (-lt[e], e))
+                assert ids[t].tolist() == expect, (E, K, logits[t], ids[t], expect)
+
+
+def pin_closed_forms_two_experts(orc):
+    """E=2: p0 = sigmoid(l0 - l1); K=2 weights are the same sigmoid; K=1 weight is 1."""
+    r = _rng(4)
+    logits = (r.standard_normal((30, 2)) * 4).astype(np.float32)
+    ids, w, probs = orc.route(logits, 2)
+    l = logits.astype(np.float64)
+    sig = 1.0 / (1.0 + np.exp(-(l[:, 0] - l[:, 1])))
+    np.testing.assert_allclose(probs[:, 0], sig, rtol=1e-14, atol=1e-16)
+    first = np.where(l[:, 0] >= l[:, 1], 0, 1)
+    assert np.array_equal(ids[:, 0], first)
+    w_first = np.where(first == 0, sig, 1 - sig)
+    np.testing.assert_allclose(w[:, 0], w_first, rtol=1e-13, atol=1e-15)
+    ids1, w1, _ = orc.route(logits, 1)
+    assert np.array_equal(ids1[:, 0], first) and np.all(w1 == 1.0)
+
+
+def pin_uniform_router(orc):
+    """A zero router gives equal logits: experts 0..K-1 in order, weights 1/K,
+    probabilities 1/E, and aux_loss exactly 1 (notes §1.2, uniform case)."""
+    T, d, E, K = 16, 12, 8, 2
+    x = _rng(5).standard_normal((T, d)).astype(np.float32)
+    wr = np.zeros((d, E), np.float32)
+    logits = orc.router_logits(x, wr)
+    assert np.all(logits == 0)
+    ids, w, probs = orc.route(logits.astype(np.float32), K)
+    assert np.all(ids == np.arange(K))
+    assert np.all(w == 1.0 / K) and np.allclose(probs, 1.0 / E, rtol=0, atol=1e-16)
+    disp = orc.dispatch(ids, E)
+    aux = orc.aux_loss(disp["counts"], probs, K)
+    assert abs(aux - 1.0) < 1e-15, aux
+
+
+def pin_router_logits_library(orc):
+    """Router scores equal numpy's float64 matmul on the exactly widened inputs
+    (non-square shapes catch a transposed operand), for fp32 and bf16 inputs."""
+    from mixture_experts_layer_38_amd.datagen import f32_to_bf16_bits, bf16_bits_to_f32
+    r = _rng(6)
+    T, d, E = 13, 24, 5
+    x = r.standard_normal((T, d)).astype(np.float32)
+    wr = r.standard_normal((d, E)).astype(np.float32)
+    got = orc.router_logits(x, wr)
+    ref = x.astype(np.float64) @ wr.astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+    xb, wb = f32_to_bf16_bits(x), f32_to_bf16_bits(wr)
+    got = orc.router_logits(xb, wb)
+    ref = bf16_bits_to_f32(xb).astype(np.float64) @ bf16_bits_to_f32(wb).astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_bias_enters_selection_and_weights(orc):
+    """The per-expert bias is added to the logits before selection and softmax
+    (engineering page §1.2): a large bias forces an expert into every token's
+    top-K, and routing with bias b equals routing the fp32 sums without bias."""
+    r = _rng(7)
+    T, E, K = 20, 8, 2
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    bias = np.zeros(E, np.float32)
+    bias[3] = 100.0
+    ids, w, _ = orc.route(logits, K, bias)
+    assert np.all(ids[:, 0] == 3)
+    assert np.all(w[:, 0] > 0.999)
+    b2 = r.uniform(-0.5, 0.5, E).astype(np.float32)
+    ids_b, w_b, p_b = orc.route(logits, K, b2)
+    summed = (logits + b2).astype(np.float32)
+    ids_n, w_n = _numpy_topk_then_softmax(summed, None, K)
+    assert np.array_equal(ids_b, ids_n)
+    np.testing.assert_allclose(w_b, w_n, rtol=0, atol=1e-12)
+
+
+def pin_k_equals_e(orc):
+    """K = E: every expert is chosen, in descending order, and the renormalised
+    weights equal the full softmax probabilities."""
+    r = _rng(8)
+    logits = r.standard_normal((9, 6)).astype(np.float32)
+    ids, w, probs = orc.route(logits, 6)
+    for t in range(9):
+        assert sorted(ids[t].tolist()) == list(range(6))
+        np.testing.assert_allclose(w[t], probs[t, ids[t]], rtol=1e-14, atol=1e-16)
+        assert np.all(np.diff(logits[t, ids[t]]) <= 0)
+
+
+# --------------------------------------------------------------------------
+# dispatch
+# --------------------------------------------------------------------------
+
+def _brute_dispatch(ids, E, C):
+    flat = ids.reshape(-1).tolist()
+    n = len(flat)
+    counts = [flat.count(e) for e in range(E)]
+    rank = [sum(1 for j in range(i) if flat[j] == flat[i]) for i in range(n)]
+    kept = [c if C < 0 else min(c, C) for c in counts]
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + kept[e])
+    assign = [offsets[flat[i]] + rank[i] if (C < 0 or rank[i] < C) else -1 for i in range(n)]
+    row_assign = [-1] * n
+    for i, a in enumerate(assign):
+        if a >= 0:
+            row_assign[a] = i
+    return counts, kept, offsets, assign, row_assign
+
+
+def pin_dispatch_bruteforce(orc):
+    """O((T*K)^2) ranks by their definition, with capacities none, 0, 1, 3, 10**6."""
+    r = _rng(9)
+    for T, E, K in ((1, 4, 2), (7, 3, 1), (23, 8, 2), (17, 5, 5), (31, 16, 4)):
+        ids = np.stack([r.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+        for C in (-1, 0, 1, 3, 10 ** 6):
+            got = orc.dispatch(ids, E, C)
+            counts, kept, offsets, assign, row_assign = _brute_dispatch(ids, E, C)
+            assert got["counts"].tolist() == counts
+            assert got["kept"].tolist() == kept
+            assert got["offsets"].tolist() == offsets
+            assert got["assign_row"].tolist() == assign
+            assert got["row_assign"].tolist() == row_assign
+
+
+def pin_dispatch_invariants(orc):
+    """Sum of counts is T*K, so the mean per expert is T*K/E (notes §3.1); kept is
+    min(count, C); assign_row and row_assign are inverse on kept assignments;
+    rows of one expert are in increasing flat order; C >= T*K equals unlimited;
+    C = 0 keeps nothing."""
+    r = _rng(10)
+    T, E, K = 200, 16, 2
+    p = np.arange(1, E + 1, dtype=np.float64) ** -1.2
+    ids = np.stack([r.choice(E, K, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    un = orc.dispatch(ids, E, -1)
+    assert un["counts"].sum() == T * K and un["counts"].mean() == T * K / E
+    for C in (0, 5, 25, T * K):
+        g = orc.dispatch(ids, E, C)
+        assert np.array_equal(g["counts"], un["counts"])
+        assert np.array_equal(g["kept"], np.minimum(un["counts"], C))
+        S = g["offsets"][-1]
+        assert S == g["kept"].sum()
+        ar, ra = g["assign_row"], g["row_assign"]
+        kept_idx = np.nonzero(ar >= 0)[0]
+        assert len(kept_idx) == S
+        assert np.array_equal(ra[ar[kept_idx]], kept_idx)
+        assert np.all(ra[S:] == -1)
+        for e in range(E):
+            rows = ra[g["offsets"][e]:g["offsets"][e + 1]]
+            assert np.all(ids.reshape(-1)[rows] == e)
+            assert np.all(np.diff(rows) > 0)
+        if C == T * K:
+            for key in ("kept", "offsets", "assign_row", "row_assign"):
+                assert np.array_equal(g[key], un[key])
+        if C == 0:
+            assert S == 0 and np.all(ar == -1)
+
+
+# --------------------------------------------------------------------------
+# experts and combine
+# --------------------------------------------------------------------------
+
+def _saturated_experts(r, E, F, d, T):
+    """Inputs whose gate pre-activations are all >= 40 or <= -40, so SiLU is the
+    identity or zero to within exp(-40) relative; numpy can then evaluate every
+    expert with plain matmuls and a 0/1 mask (no SiLU formula needed)."""
+    x = r.uniform(-1, 1, (T, d)).astype(np.float32)
+    x[:, -1] = 1.0
+    w1 = (r.uniform(-1, 1, (E, F, d)) * (2.0 / d)).astype(np.float32)
+    sign = r.choice([-1.0, 1.0], size=(E, F)).astype(np.float32)
+    w1[:, :, -1] = sign * 60.0
+    w3 = r.standard_normal((E, F, d)).astype(np.float32)
+    w2 = r.standard_normal((E, d, F)).astype(np.float32)
+    mask = (sign > 0).astype(np.float64)
+
+    def ref_expert(e, xt):
+        g1 = w1[e].astype(np.float64) @ xt.astype(np.float64)
+        g3 = w3[e].astype(np.float64) @ xt.astype(np.float64)
+        return w2[e].astype(np.float64) @ (mask[e] * g1 * g3)
+    return x, w1, w3, w2, ref_expert
+
+
+def pin_expert_library(orc):
+    """Expert FFN against numpy matmuls (d != F catches transposed operands), with
+    the gate saturated so SiLU is exactly identity or zero; plus SiLU(0) = 0."""
+    r = _rng(11)
+    E, F, d, T = 3, 7, 5, 4
+    x, w1, w3, w2, ref_expert = _saturated_experts(r, E, F, d, T)
+    for e in range(E):
+        for t in range(T):
+            got = orc.expert(x[t], w1[e], w3[e], w2[e])
+            ref = ref_expert(e, x[t])
+            np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    zero = orc.expert(x[0], np.zeros_like(w1[0]), w3[0], w2[0])
+    assert np.all(zero == 0.0)
+
+
+def pin_dense_masked_combine(orc):
+    """Computing every expert for every token and weighting by the K-sparse
+    weights (zero for unselected experts, notes §2.2) equals the sparse result;
+    dropped assignments contribute nothing."""
+    r = _rng(12)
+    E, F, d, T, K = 6, 9, 7, 15, 2
+    x, w1, w3, w2, ref_expert = _saturated_experts(r, E, F, d, T)
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    ids, w, _ = orc.route(logits, K)
+    for C in (-1, 3):
+        disp = orc.dispatch(ids, E, C)
+        y = orc.layer_output(x, w1, w3, w2, ids, w, disp["assign_row"])
+        dense_w = np.zeros((T, E))
+        for t in range(T):
+            for k in range(K):
+                if disp["assign_row"][t * K + k] >= 0:
+                    dense_w[t, ids[t, k]] = w[t, k]
+        ref = np.zeros((T, d))
+        for t in range(T):
+            for e in range(E):
+                ref[t] += dense_w[t, e] * ref_expert(e, x[t])
+        np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-11)
+
+
+def pin_identical_experts(orc):
+    """With every expert identical the weighted sum is that expert's output for
+    every token, whatever the routing (the K weights sum to one)."""
+    r = _rng(13)
+    E, F, d, T, K = 4, 6, 5, 9, 2
+    x = r.standard_normal((T, d)).astype(np.float32)
+    one1 = r.standard_normal((F, d)).astype(np.float32)
+    one3 = r.standard_normal((F, d)).astype(np.float32)
+    one2 = r.standard_normal((d, F)).astype(np.float32)
+    w1 = np.repeat(one1[None], E, 0)
+    w3 = np.repeat(one3[None], E, 0)
+    w2 = np.repeat(one2[None], E, 0)
+    ids, w, _ = orc.route(r.standard_normal((T, E)).astype(np.float32), K)
+    y = orc.layer_output(x, w1, w3, w2, ids, w)
+    for t in range(T):
+        np.testing.assert_allclose(y[t], orc.expert(x[t], one1, one3, one2), rtol=1e-12, atol=1e-12)
+
+
+def pin_capacity_zero(orc):
+    """Capacity 0 drops every assignment, so the layer output is exactly zero."""
+    r = _rng(14)
+    E, F, d, T, K = 4, 6, 5, 9, 2
+    x = r.standard_normal((T, d)).astype(np.float32)
+    w1 = r.standard_normal((E, F, d)).astype(np.float32)
+    w3 = r.standard_normal((E, F, d)).astype(np.float32)
+    w2 = r.standard_normal((E, d, F)).astype(np.float32)
+    ids, w, _ = orc.route(r.standard_normal((T, E)).astype(np.float32), K)
+    disp = orc.dispatch(ids, E, 0)
+    y = orc.layer_output(x, w1, w3, w2, ids, w, disp["assign_row"])
+    assert np.all(y == 0.0)
+
+
+def pin_silu_closed_forms(orc):
+    """SiLU(z) = z / (1 + e^-z) at z = 1, -1, 2 through a 1x1 expert:
+    h = w2 * SiLU(w1 x) * (w3 x) with x = 1, w3 = w2 = 1."""
+    e = math.e
+    for z, expect in ((1.0, e / (1 + e)), (-1.0, -1 / (1 + e)), (2.0, 2 / (1 + math.exp(-2.0)))):
+        h = orc.expert(np.array([1.0], np.float32), np.array([[z]], np.float32),
+                       np.array([[1.0]], np.float32), np.array([[1.0]], np.float32))
+        assert abs(h[0] - expect) < 1e-15, (z, h, expect)
+
+
+# --------------------------------------------------------------------------
+# aux loss and bias update
+# --------------------------------------------------------------------------
+
+def pin_aux_loss_hand_cases(orc):
+    """Hand-worked cases of aux = N * sum f_i P_i (notes §1.2)."""
+    g = _golden("aux_loss_hand.json")
+    for c in g["cases"]:
+        aux = orc.aux_loss(np.array(c["counts"], np.int32), np.array(c["probs"]), c["K"])
+        assert abs(aux - c["expect_aux"]) < 1e-15, (aux, c)
+
+
+def pin_aux_loss_uniform_load(orc):
+    """Uniform choice fractions f_i = 1/N give aux = sum_i P_i = 1 exactly for any
+    probabilities; the load-relative reading N*aux equals N."""
+    r = _rng(15)
+    T, E, K = 8, 4, 2
+    probs = r.dirichlet(np.ones(E), size=T)
+    counts = np.full(E, T * K // E, np.int32)
+    aux = orc.aux_loss(counts, probs, K)
+    assert abs(aux - 1.0) < 1e-14 and abs(E * aux - E) < 1e-13
+
+
+def pin_bias_update_sign_rule(orc):
+    """Engineering page §1.2: overloaded experts lose alpha, underloaded gain it,
+    experts at exactly the average T*K/E keep their bias."""
+    T, K, E, alpha = 8, 2, 4, np.float32(1e-3)
+    counts = np.array([7, 4, 4, 1], np.int32)        # target 4
+    bias0 = np.array([0.5, -0.25, 0.0, 1.0], np.float32)
+    got = orc.bias_update(counts, T, K, float(alpha), bias0)
+    expect = np.array([bias0[0] - alpha, bias0[1], bias0[2], bias0[3] + alpha], np.float32)
+    assert np.array_equal(got, expect), (got, expect)
+    r = _rng(16)
+    for _ in range(20):
+        counts = r.integers(0, 9, E).astype(np.int32)
+        got = orc.bias_update(counts, T, K, float(alpha), np.zeros(E, np.float32))
+        for e in range(E):
+            want = -alpha if counts[e] * E > T * K else (alpha if counts[e] * E < T * K else 0)
+            assert got[e] == np.float32(want)
+        n_under = int((counts * E < T * K).sum())
+        n_over = int((counts * E > T * K).sum())
+        assert abs(float(got.astype(np.float64).sum()) - float(alpha) * (n_under - n_over)) < 1e-9
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
