@@ -1,0 +1,205 @@
+"""MoE-layer forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config mixtral_decode]
+
+One step is one moe_forward call (router, dispatch, grouped SwiGLU FFN,
+combine) over one batch of seeded synthetic tokens whose inputs and weights
+are already resident in HBM.  The headline line is the Mixtral-8x7B-shaped
+decode step (T=32, d=4096, E=8, K=2, F=14336, bf16); the prefill step
+(T=8192, Zipf(1.2) routing skew) runs on the same resident weights and is
+reported in the "prefill" object.  The CPU oracle is timed on a bounded
+sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec, Mixtral shape decode+prefill; % HBM / MFMA peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    kdir = os.path.join(ROOT, "mixture_experts_layer_38_amd", "csrc", "kernels")
+    for f in sorted(os.listdir(kdir)):
+        if f.startswith("ffn"):
+            with open(os.path.join(kdir, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def gate_up_algorithmic(cfg, counts_kept: np.ndarray):
+    """Algorithmic bytes and flops of one gate/up launch: the W1 and W3 rows of
+    every expert with at least one kept row, each read once, plus the grouped
+    token rows read and the activation rows written."""
+    S = int(counts_kept.sum())
+    active = int((counts_kept > 0).sum())
+    b = cfg.elem_bytes
+    bytes_ = active * 2 * cfg.F * cfg.d * b + S * cfg.d * b + S * cfg.F * b
+    flops = 2.0 * S * 2 * cfg.d * cfg.F
+    return bytes_, flops
+
+
+def layer_algorithmic(cfg, counts_kept: np.ndarray):
+    """Algorithmic bytes and flops of the whole layer (router + experts)."""
+    S = int(counts_kept.sum())
+    active = int((counts_kept > 0).sum())
+    b = cfg.elem_bytes
+    bytes_ = active * 3 * cfg.F * cfg.d * b + 2 * cfg.T * cfg.d * b + cfg.d * cfg.E * b
+    flops = 2.0 * cfg.T * cfg.d * cfg.E + 2.0 * S * 3 * cfg.d * cfg.F
+    return bytes_, flops
+
+
+def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str):
+    import torch
+    import mixture_experts_layer_38_amd as moe
+    y = torch.empty((cfg.T, cfg.d), dtype=layer.torch_dtype, device="cuda")
+    dbg = layer.alloc_debug()
+    layer.forward(x, bias, y=y, dbg=dbg)
+    torch.cuda.synchronize()
+    kept = dbg["kept"].cpu().numpy()
+    counts = dbg["counts"].cpu().numpy()
+    for _ in range(warmup):
+        layer.forward(x, bias, y=y)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in starts + stops:  # materialise the underlying hipEvent_t
+        e.record()
+    torch.cuda.synchronize()
+    keep = moe.moe_set_kernel_timer(kernel, starts, stops)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, bias, y=y)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_rec = moe.moe_kernel_timer_count(kernel)
+    moe.moe_set_kernel_timer(kernel, [], [])
+    del keep
+    kern_ms = [starts[i].elapsed_time(stops[i]) for i in range(n_rec)]
+    return wall, float(np.mean(kern_ms)) if kern_ms else float("nan"), counts, kept
+
+
+def cpu_baseline(cfg, inp, n_tokens: int):
+    import oracle
+    orc = oracle.get()
+    toks = np.arange(n_tokens, dtype=np.int64)
+    x = np.ascontiguousarray(inp["x"][:n_tokens])
+    t0 = time.perf_counter()
+    orc.forward(x, inp["w_router"], inp["w1"], inp["w3"], inp["w2"], cfg.K,
+                inp["logit_bias"], cfg.capacity, toks)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": orc.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"{n_tokens} tokens of {cfg.name} (full routing, grouping and "
+                      f"fp64 SwiGLU experts + combine for every sampled token)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_decode")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_layer_38_amd as moe
+    from mixture_experts_layer_38_amd import datagen
+    from mixture_experts_layer_38_amd.configs import CONFIGS
+    from mixture_experts_layer_38_amd.layer import MoELayer, to_device
+
+    moe.load()
+    cfg = CONFIGS[args.config]
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    inp = datagen.make_inputs(cfg)
+    layer = MoELayer.from_host(cfg, inp)
+    x = to_device(inp["x"], cfg.dtype)
+    bias = None if inp["logit_bias"] is None else torch.from_numpy(inp["logit_bias"]).cuda()
+    print("[bench] timing", file=sys.stderr, flush=True)
+    wall, k_ms, counts, kept = time_workload(cfg, layer, x, bias, args.steps, args.warmup, "ffn_gate_up")
+    ms_step = wall / args.steps * 1e3
+    tok_s = cfg.T * args.steps / wall
+    gb, gf = gate_up_algorithmic(cfg, kept)
+    lb, lf = layer_algorithmic(cfg, kept)
+    achieved = gb / (k_ms * 1e-3) / 1e9
+    traffic = load_traffic(cfg.name, "ffn_gate_up")
+    result = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} K={cfg.K} "
+                               f"F={cfg.F} {cfg.dtype}", "T": cfg.T, "d_model": cfg.d,
+                   "experts": cfg.E, "top_k": cfg.K, "d_ff": cfg.F, "capacity": cfg.capacity},
+        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel_ms": k_ms, "algorithmic_bytes": gb},
+        "layer": {"hbm_frac": lb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "algorithmic_bytes": lb, "algorithmic_flops": lf,
+                  "counts": counts.tolist()},
+    }
+    if not args.no_prefill and cfg.name == "mixtral_decode":
+        pcfg = CONFIGS["mixtral_prefill"]
+        pin = datagen.make_inputs(pcfg, with_experts=False)
+        player = MoELayer(pcfg.T, pcfg.d, pcfg.E, pcfg.K, pcfg.F, pcfg.dtype, layer.w_router,
+                          layer.w1, layer.w3, layer.w2, pcfg.capacity)
+        px = to_device(pin["x"], pcfg.dtype)
+        pb = torch.from_numpy(pin["logit_bias"]).cuda()
+        print("[bench] timing prefill", file=sys.stderr, flush=True)
+        pwall, pk_ms, pcounts, pkept = time_workload(pcfg, player, px, pb, args.prefill_steps, 2,
+                                                     "ffn_gate_up")
+        pgb, pgf = gate_up_algorithmic(pcfg, pkept)
+        plb, plf = layer_algorithmic(pcfg, pkept)
+        pms = pwall / args.prefill_steps * 1e3
+        result["prefill"] = {
+            "workload": f"{pcfg.name}: T={pcfg.T} Zipf({pcfg.zipf_s}) skew",
+            "value": pcfg.T * args.prefill_steps / pwall, "unit": "tokens/s", "ms_per_step": pms,
+            "steps": args.prefill_steps,
+            "roofline": {"bound": "mfma", "kernel": "ffn_gate_up",
+                         "achieved": pgf / (pk_ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": pgf / (pk_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+                         "traffic": load_traffic(pcfg.name, "ffn_gate_up"), "kernel_ms": pk_ms},
+            "layer_mfma_frac": plf / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+            "counts": pcounts.tolist(),
+        }
+        del player, px
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, min(cfg.T, 32))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

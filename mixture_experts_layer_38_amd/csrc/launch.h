@@ -1,0 +1,56 @@
+// Host-side launch wrappers of the MoE kernels (internal to libmoe.so).
+// Shapes have been validated by the C ABI layer before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---- kernel timing hook ----------------------------------------------------
+void timer_before(int kid, hipStream_t s);
+void timer_after(int kid, hipStream_t s);
+
+// Launch `expr` (a kernel launch) bracketed by the timing hook of kernel `kid`.
+#define MOE_TIMED_LAUNCH(kid, stream, ...)        \
+    do {                                          \
+        ::moe::timer_before((kid), (stream));     \
+        __VA_ARGS__;                              \
+        ::moe::timer_after((kid), (stream));      \
+    } while (0)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- router ----------------------------------------------------------------
+// Number of token blocks the router uses (its prob_sum partials are per block).
+int router_num_blocks(int T, int dtype);
+size_t router_ws_bytes(int T, int E, int dtype);
+hipError_t launch_router(int T, int d, int E, int K, int dtype, const void* x,
+                         const void* w_router, const float* bias, float* logits, float* probs,
+                         float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s);
+
+// ---- dispatch --------------------------------------------------------------
+size_t dispatch_ws_bytes(int T, int K, int E);
+hipError_t launch_dispatch(int T, int K, int E, int d, int dtype, int capacity,
+                           const int32_t* ids, const void* x, int32_t* counts, int32_t* kept,
+                           int32_t* offsets, int32_t* assign_row, int32_t* row_assign,
+                           void* x_perm, void* ws, hipStream_t s);
+
+// ---- grouped expert FFN ----------------------------------------------------
+size_t ffn_ws_bytes(int T, int K, int E, int d, int F, int dtype);
+hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* x_perm,
+                      const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                      void* act, void* h, void* ws, hipStream_t s);
+
+// ---- combine / aux / bias --------------------------------------------------
+hipError_t launch_combine(int T, int K, int d, int dtype, const void* h,
+                          const int32_t* assign_row, const float* w, void* y, hipStream_t s);
+hipError_t launch_aux(int T, int K, int E, const int32_t* counts, const float* prob_sum,
+                      float* aux, hipStream_t s);
+hipError_t launch_bias_update(int T, int K, int E, const int32_t* counts, float alpha,
+                              float* bias, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,107 @@
+"""Shared pieces of the GPU parity tests: run the HIP path through the C ABI,
+then check its results against the CPU oracle.
+
+Compare rules:
+  - integer work (expert ids, counts, kept, offsets, both row maps) bit-exact,
+    with the oracle routing the GPU's own fp32 logits;
+  - routing weights |w - w_oracle| <= 1e-6; GPU logits against the oracle's
+    fp64 logits ||d||_inf / ||L||_inf <= 1e-4 (a diagnostic of the router GEMM);
+  - layer output: fp32 ||d||_inf / ||y||_inf <= 1e-4, bf16 ||d||_2 / ||y||_2
+    <= 1e-2 against the fp64 oracle on the same bf16-rounded inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from mixture_experts_layer_38_amd import datagen
+from mixture_experts_layer_38_amd.configs import MoEConfig
+from mixture_experts_layer_38_amd.layer import MoELayer, to_device, to_host
+
+TOL_W = 1e-6
+TOL_LOGITS = 1e-4
+TOL_Y_F32 = 1e-4
+TOL_Y_BF16 = 1e-2
+TOL_AUX = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_forward(cfg: MoEConfig, inp: dict, logit_bias: np.ndarray | None = None, repeat: int = 1):
+    """moe_forward with every debug output; returns host arrays (and the layer)."""
+    import torch
+    layer = MoELayer.from_host(cfg, inp)
+    x = to_device(inp["x"], cfg.dtype)
+    lb = inp["logit_bias"] if logit_bias is None else logit_bias
+    bias = None if lb is None else torch.from_numpy(np.ascontiguousarray(lb, np.float32)).cuda()
+    outs = []
+    for _ in range(repeat):
+        dbg = layer.alloc_debug()
+        y = layer.forward(x, bias, dbg=dbg)
+        torch.cuda.synchronize()
+        host = {k: v.cpu().numpy() for k, v in dbg.items()}
+        host["y"] = to_host(y, cfg.dtype)
+        outs.append(host)
+    return outs if repeat > 1 else outs[0], layer
+
+
+def y_as_f64(y: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return datagen.bf16_bits_to_f32(y).astype(np.float64)
+    return y.astype(np.float64)
+
+
+def check_logits(orc, inp, gpu_logits, tokens=None):
+    x = inp["x"] if tokens is None else np.ascontiguousarray(inp["x"][tokens])
+    ref = orc.router_logits(x, inp["w_router"])
+    got = gpu_logits if tokens is None else gpu_logits[tokens]
+    err = np.abs(got.astype(np.float64) - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err <= TOL_LOGITS, f"router logits rel-inf error {err:.3e}"
+    return err
+
+
+def check_routing(orc, cfg: MoEConfig, out: dict, bias):
+    """Bit-exact ids from the GPU's logits; weights within TOL_W; probabilities."""
+    ids, w, probs = orc.route(out["logits"], cfg.K, bias)
+    bad = np.nonzero((ids != out["topk_ids"]).any(1))[0]
+    assert len(bad) == 0, f"{len(bad)} tokens with different expert ids, first {bad[:5]}"
+    dw = np.abs(out["topk_w"].astype(np.float64) - w).max()
+    assert dw <= TOL_W, f"routing weight error {dw:.3e}"
+    dp = np.abs(out["probs"].astype(np.float64) - probs).max()
+    assert dp <= TOL_W, f"probability error {dp:.3e}"
+    return ids, w, probs
+
+
+def check_dispatch(orc, cfg: MoEConfig, ids, out: dict, capacity: int):
+    ref = orc.dispatch(ids, cfg.E, capacity)
+    for key in ("counts", "kept", "offsets", "assign_row", "row_assign"):
+        got = out[key].reshape(-1)
+        if not np.array_equal(got, ref[key]):
+            where = np.nonzero(got != ref[key])[0]
+            raise AssertionError(f"{key} differs at {len(where)} positions, first {where[:5]}: "
+                                 f"gpu {got[where[:5]]} oracle {ref[key][where[:5]]}")
+    return ref
+
+
+def check_output(orc, cfg: MoEConfig, inp: dict, ids, w, assign_row, y_gpu, tokens=None):
+    y_ref = orc.layer_output(inp["x"], inp["w1"], inp["w3"], inp["w2"], ids, w, assign_row, tokens)
+    y = y_as_f64(y_gpu, cfg.dtype)
+    if tokens is not None:
+        y = y[tokens]
+    if cfg.dtype == "f32":
+        err = np.abs(y - y_ref).max() / max(np.abs(y_ref).max(), 1e-30)
+        assert err <= TOL_Y_F32, f"fp32 output rel-inf error {err:.3e}"
+    else:
+        err = np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-30)
+        assert err <= TOL_Y_BF16, f"bf16 output rel-L2 error {err:.3e}"
+    return err
+
+
+def load_summary(cfg: MoEConfig, out: dict) -> str:
+    counts = out["counts"]
+    avg = cfg.T * cfg.K / cfg.E
+    lg = out["logits"]
+    return (f"counts max/avg {counts.max() / avg:.2f} min {counts.min()} max {counts.max()} "
+            f"kept S={int(out['offsets'][-1])} logits mean {lg.mean():.3f} std {lg.std():.3f} "
+            f"min {lg.min():.3f} max {lg.max():.3f}")

@@ -1,0 +1,134 @@
+"""Per-step parity through the separate C-ABI calls (moe_route, moe_dispatch,
+moe_expert_ffn, moe_combine) against the CPU oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import mixture_experts_layer_38_amd as moe
+from mixture_experts_layer_38_amd import datagen
+from mixture_experts_layer_38_amd.configs import CONFIGS, scaled
+from mixture_experts_layer_38_amd.layer import to_device, to_host
+from tests.gpu_harness import TOL_W, say, y_as_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def _t(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _empty(shape, dtype):
+    import torch
+    return torch.empty(shape, dtype=dtype, device="cuda")
+
+
+@pytest.mark.parametrize("E,K,with_bias", [(8, 2, False), (8, 1, True), (64, 2, True),
+                                            (256, 8, True), (5, 5, False), (1000, 7, True)])
+def test_route_given_logits_with_ties(orc, E, K, with_bias):
+    """x = NULL mode: the GPU routes logits chosen by the test, full of exact
+    ties and signed zeros; ids must match the oracle bit for bit."""
+    import torch
+    say(f"[case] route ties E={E} K={K} bias={with_bias}")
+    rng = np.random.default_rng(E * 100 + K)
+    T = 333
+    vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0, 2.0], np.float32)
+    logits = rng.choice(vals, size=(T, E)).astype(np.float32)
+    bias = None
+    if with_bias:
+        bias = rng.choice(np.array([-0.0, 0.0, 0.5, -0.5], np.float32), size=E).astype(np.float32)
+    p = moe.problem(T, 64, E, K, 64, "bf16")
+    lg = _t(logits)
+    ids = _empty((T, K), torch.int32)
+    w = _empty((T, K), torch.float32)
+    probs = _empty((T, E), torch.float32)
+    psum = _empty((E,), torch.float32)
+    ws = _empty((moe.moe_route_workspace_size(p),), torch.uint8)
+    moe.moe_route(p, None, None, None if bias is None else _t(bias), lg, probs, psum, ids, w, ws)
+    torch.cuda.synchronize()
+    ids_ref, w_ref, p_ref = orc.route(logits, K, bias)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= TOL_W
+    assert np.abs(probs.cpu().numpy() - p_ref).max() <= TOL_W
+    assert np.abs(psum.cpu().numpy() - p_ref.sum(0)).max() <= 1e-5
+
+
+@pytest.mark.parametrize("T,E,K,cap", [(1, 8, 2, -1), (5, 1, 1, -1), (1000, 8, 2, -1), (1000, 8, 2, 100),
+                                       (5000, 64, 2, 7), (4096, 256, 8, -1), (3000, 1024, 4, 3),
+                                       (777, 16, 4, 0), (2500, 3, 2, 1)])
+def test_dispatch_oracle_ids(orc, T, E, K, cap):
+    """Dispatch of skewed ids picked by the test: counts, kept, offsets and both
+    row maps bit-exact; gathered rows are exact copies of x."""
+    import torch
+    say(f"[case] dispatch T={T} E={E} K={K} C={cap}")
+    rng = np.random.default_rng(T + E)
+    pr = np.arange(1, E + 1, dtype=np.float64) ** -1.1
+    pr /= pr.sum()
+    ids = np.stack([rng.choice(E, K, replace=False, p=pr) for _ in range(T)]).astype(np.int32)
+    d = 72
+    x = datagen.normal(5, 1, (T, d), 1.0, "bf16")
+    p = moe.problem(T, d, E, K, 64, "bf16", cap)
+    n = T * K
+    outs = {k: _empty(s, torch.int32) for k, s in
+            (("counts", (E,)), ("kept", (E,)), ("offsets", (E + 1,)), ("assign_row", (n,)),
+             ("row_assign", (n,)))}
+    x_perm = _empty((n, d), torch.bfloat16)
+    ws = _empty((moe.moe_dispatch_workspace_size(p),), torch.uint8)
+    moe.moe_dispatch(p, _t(ids), to_device(x, "bf16"), outs["counts"], outs["kept"], outs["offsets"],
+                     outs["assign_row"], outs["row_assign"], x_perm, ws)
+    torch.cuda.synchronize()
+    ref = orc.dispatch(ids, E, cap)
+    for k, v in outs.items():
+        assert np.array_equal(v.cpu().numpy(), ref[k]), k
+    S = int(ref["offsets"][-1])
+    xp = to_host(x_perm, "bf16")[:S]
+    assert np.array_equal(xp, x[ref["row_assign"][:S] // K])
+
+
+@pytest.mark.parametrize("name,T,d,F", [("decode", 32, 256, 1032), ("prefill", 700, 264, 200),
+                                        ("fp32", 50, 64, 48)])
+def test_ffn_and_combine_steps(orc, name, T, d, F):
+    """moe_expert_ffn on grouped rows, then moe_combine, against per-row oracle
+    experts and the oracle layer output."""
+    import torch
+    E, K = 8, 2
+    dt = "f32" if name == "fp32" else "bf16"
+    say(f"[case] ffn+combine {name} T={T} d={d} F={F}")
+    cfg = scaled(CONFIGS["mixtral_prefill"], T=T, d=d, F=F, E=E, K=K, dtype=dt)
+    inp = datagen.make_inputs(cfg)
+    rng = np.random.default_rng(7)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w, _ = orc.route(logits, K, inp["logit_bias"])
+    ref = orc.dispatch(ids, E, -1)
+    S = int(ref["offsets"][-1])
+    x_perm = inp["x"][ref["row_assign"] // K]
+    p = moe.problem(T, d, E, K, F, dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    act = _empty((T * K, F), tdt)
+    h = _empty((T * K, d), tdt)
+    y = _empty((T, d), tdt)
+    ws = _empty((moe.moe_expert_ffn_workspace_size(p),), torch.uint8)
+    moe.moe_expert_ffn(p, to_device(x_perm, dt), _t(ref["offsets"]), to_device(inp["w1"], dt),
+                       to_device(inp["w3"], dt), to_device(inp["w2"], dt), act, h, ws)
+    moe.moe_combine(p, h, _t(ref["assign_row"]), _t(w.astype(np.float32)), y)
+    torch.cuda.synchronize()
+    h_gpu = y_as_f64(to_host(h, dt), dt)[:S]
+    h_ref = np.empty((S, d))
+    for r in range(S):
+        t = ref["row_assign"][r] // K
+        e = int(np.searchsorted(ref["offsets"], r, side="right") - 1)
+        h_ref[r] = orc.expert(inp["x"][t], inp["w1"][e], inp["w3"][e], inp["w2"][e])
+    err_h = np.linalg.norm(h_gpu - h_ref) / np.linalg.norm(h_ref)
+    y_ref = orc.layer_output(inp["x"], inp["w1"], inp["w3"], inp["w2"], ids, w, ref["assign_row"])
+    y_gpu = y_as_f64(to_host(y, dt), dt)
+    err_y = np.linalg.norm(y_gpu - y_ref) / np.linalg.norm(y_ref)
+    say(f"    h rel-L2 {err_h:.3e}  y rel-L2 {err_y:.3e}")
+    tol = 1e-4 if dt == "f32" else 1e-2
+    assert err_h <= tol and err_y <= tol
