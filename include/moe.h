@@ -104,8 +104,9 @@ const char* moe_status_string(moe_status s);
 /* Library version string. */
 const char* moe_version(void);
 
-/* Workspace bytes needed by moe_route (only when prob_sum is requested),
- * moe_dispatch, moe_expert_ffn and moe_forward for problem `p`. */
+/* Workspace bytes needed by moe_route (when it computes bf16 scores from x,
+ * or when prob_sum is requested), moe_dispatch, moe_expert_ffn and
+ * moe_forward for problem `p`. */
 moe_status moe_route_workspace_size(const moe_problem* p, size_t* bytes);
 moe_status moe_dispatch_workspace_size(const moe_problem* p, size_t* bytes);
 moe_status moe_expert_ffn_workspace_size(const moe_problem* p, size_t* bytes);
@@ -121,8 +122,10 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
  *              softmax and the top-K
  *   logits     [T, E] fp32, out (in when x is NULL): x W_r, fp32 accumulation
  *   probs      [T, E] fp32 or NULL: softmax over all E of logits + bias
- *   prob_sum   [E] fp32 or NULL: sum over tokens of probs (fixed order);
- *              needs ws of moe_route_workspace_size bytes
+ *   prob_sum   [E] fp32 or NULL: sum over tokens of probs (fixed order)
+ *   ws         scratch of moe_route_workspace_size bytes; required when x is
+ *              given with dtype bf16 or when prob_sum is requested, else may
+ *              be NULL
  *   topk_ids   [T, K] int32: experts by (l' descending, index ascending);
  *              -0.0 and +0.0 compare equal
  *   topk_w     [T, K] fp32: p[id_k] / sum_j p[id_j] */

@@ -1,8 +1,8 @@
 // Combine, aux loss and bias update.
 //  combine: MoE notes (www.cf-1.com/news/5905749) §2 step 4 and §2.3 -- the
 //           output is the routing-weighted sum of the chosen experts' outputs,
-//           put back in token order; one wave per token, 16-byte vectors, k in
-//           ascending order, fp32 accumulation.
+//           put back in token order; 16-byte vectors, k in ascending order,
+//           fp32 accumulation.
 //  aux:     same notes §1.2, aux = E * sum_e f_e P_e.
 //  bias:    engineering page (ybb.press/quantum-computing/18594) §1.2, one
 //           +-alpha step toward the average load T*K/E.
@@ -11,6 +11,9 @@
 
 namespace moe {
 
+// One thread per 16-byte vector of one output row: thread i handles token
+// i / (d / VEC), columns VEC * (i % (d / VEC)) ..; all loads of a thread are
+// independent, so short and long token counts both fill the chip.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(int n_tok, int K, int d,
                                                      const T* __restrict__ h,
@@ -18,28 +21,28 @@ __global__ __launch_bounds__(256) void combine_kernel(int n_tok, int K, int d,
                                                      const float* __restrict__ w,
                                                      T* __restrict__ y) {
     constexpr int VEC = 16 / sizeof(T);
-    const int t = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
-    if (t >= n_tok) return;
-    const int lane = lane_id();
-    for (int c = lane * VEC; c < d; c += kWave * VEC) {
-        float acc[VEC];
+    const int per_tok = d / VEC;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)n_tok * per_tok) return;
+    const int t = (int)(i / per_tok);
+    const int c = (int)(i - (size_t)t * per_tok) * VEC;
+    float acc[VEC];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const int r = assign_row[(size_t)t * K + k];
-            if ((unsigned)r >= (unsigned)(n_tok * K)) continue;  // dropped (-1)
-            const float wk = w[(size_t)t * K + k];
-            const u32x4 raw = load16(h + (size_t)r * d + c);
-            const T* v = reinterpret_cast<const T*>(&raw);
+    for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const int r = assign_row[(size_t)t * K + k];
+        if ((unsigned)r >= (unsigned)(n_tok * K)) continue;  // dropped (-1)
+        const float wk = w[(size_t)t * K + k];
+        const u32x4 raw = load16(h + (size_t)r * d + c);
+        const T* v = reinterpret_cast<const T*>(&raw);
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) acc[j] = fmaf(wk, to_f32(v[j]), acc[j]);
-        }
-        u32x4 outv;
-        T* o = reinterpret_cast<T*>(&outv);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) o[j] = from_f32<T>(acc[j]);
-        store16(y + (size_t)t * d + c, outv);
+        for (int j = 0; j < VEC; ++j) acc[j] = fmaf(wk, to_f32(v[j]), acc[j]);
     }
+    u32x4 outv;
+    T* o = reinterpret_cast<T*>(&outv);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) o[j] = from_f32<T>(acc[j]);
+    store16(y + (size_t)t * d + c, outv);
 }
 
 __global__ __launch_bounds__(1024) void aux_kernel(int T, int K, int E,
@@ -76,7 +79,8 @@ __global__ __launch_bounds__(256) void bias_update_kernel(int T, int K, int E,
 
 hipError_t launch_combine(int T, int K, int d, int dtype, const void* h,
                           const int32_t* assign_row, const float* w, void* y, hipStream_t s) {
-    const unsigned grid = (unsigned)((T + 3) / 4);
+    const size_t vecs = (size_t)T * d / (dtype == MOE_DTYPE_F32 ? 4 : 8);
+    const unsigned grid = (unsigned)((vecs + 255) / 256);
     if (dtype == MOE_DTYPE_F32)
         MOE_TIMED_LAUNCH(MOE_KERNEL_COMBINE, s,
                          combine_kernel<float><<<grid, 256, 0, s>>>(T, K, d, (const float*)h,

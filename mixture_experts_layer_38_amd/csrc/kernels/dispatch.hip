@@ -14,6 +14,8 @@
 //             base + earlier lanes with that id; the last lane of the group
 //             advances the per-expert base in LDS;
 //   gather  : one wave per grouped row copies x[t] with 16-byte loads.
+// Up to DS_SMALL_MAX assignments (decode-sized batches), count, scan and
+// scatter run as one workgroup instead (same arithmetic, one launch).
 #include "../device_common.h"
 #include "../launch.h"
 
@@ -132,6 +134,95 @@ __global__ __launch_bounds__(kWave) void dispatch_scatter_kernel(
     for (int j = max(beg, S) + lane; j < end; j += kWave) row_assign[j] = -1;
 }
 
+constexpr int DS_SMALL_MAX = 4096;
+
+// Exclusive scan over the 1024 threads of a block (wave scans, then the wave
+// totals in order).  Returns this thread's exclusive prefix; *total gets the sum.
+__device__ __forceinline__ int block_exscan_1024(int v, int* wave_tot, int* total) {
+    const int lane = lane_id();
+    const int wv = threadIdx.x / kWave;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(incl, o);
+        if (lane >= o) incl += u;
+    }
+    if (lane == kWave - 1) wave_tot[wv] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < 1024 / kWave; ++w) {
+        if (w < wv) before += wave_tot[w];
+        all += wave_tot[w];
+    }
+    *total = all;
+    return before + incl - v;
+}
+
+// count + scan + scatter of at most DS_SMALL_MAX assignments in one block of
+// 1024 threads (thread e owns expert e in the scan).
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(
+    int n, int E, int nbits, int capacity, const int32_t* __restrict__ ids,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ assign_row, int32_t* __restrict__ row_assign) {
+    __shared__ int hist[1024];
+    __shared__ int offs[1024];
+    __shared__ int wave_tot[1024 / kWave];
+    const int tid = threadIdx.x;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) {
+        const int e = ids[i];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    const int c = tid < E ? hist[tid] : 0;
+    const int kp = tid < E ? (capacity < 0 ? c : min(c, capacity)) : 0;
+    int S = 0;
+    const int excl = block_exscan_1024(kp, wave_tot, &S);
+    if (tid < E) {
+        counts[tid] = c;
+        kept[tid] = kp;
+        offsets[tid] = excl;
+        offs[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = S;
+    hist[tid] = 0;  // from here on: running rank per expert
+    __syncthreads();
+    if (tid < kWave) {
+        const int lane = tid;
+        const unsigned long long below = (1ull << lane) - 1ull;
+        for (int base = 0; base < n; base += kWave) {
+            const int i = base + lane;
+            const bool in = i < n;
+            const int e = in ? ids[i] : -1;
+            const bool ok = in && (unsigned)e < (unsigned)E;
+            unsigned long long peers = __ballot(ok);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = ok && ((e >> b) & 1);
+                const unsigned long long bb = __ballot(bit);
+                peers &= bit ? bb : ~bb;
+            }
+            if (ok) {
+                const int r0 = hist[e];
+                const int rank = r0 + __popcll(peers & below);
+                const int last = 63 - __clzll(peers);
+                if (capacity < 0 || rank < capacity) {
+                    const int row = offs[e] + rank;
+                    assign_row[i] = row;
+                    if ((unsigned)row < (unsigned)n) row_assign[row] = i;
+                } else {
+                    assign_row[i] = -1;
+                }
+                if (lane == last) hist[e] = r0 + __popcll(peers);
+            } else if (in) {
+                assign_row[i] = -1;
+            }
+        }
+    }
+    // Rows past the kept total S carry no assignment (disjoint from the rows above).
+    for (int j = S + tid; j < n; j += 1024) row_assign[j] = -1;
+}
+
 __global__ __launch_bounds__(DS_THREADS) void dispatch_gather_kernel(
     int T, int K, int row_bytes, const int32_t* __restrict__ total,
     const int32_t* __restrict__ row_assign, const char* __restrict__ x, char* __restrict__ x_perm) {
@@ -156,17 +247,24 @@ hipError_t launch_dispatch(int T, int K, int E, int d, int dtype, int capacity,
     int32_t* blk = reinterpret_cast<int32_t*>(ws);
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    MOE_TIMED_LAUNCH(MOE_KERNEL_DISPATCH_COUNT, s,
-                     dispatch_count_kernel<<<nblk, DS_THREADS, (size_t)E * 4, s>>>(n, E, ch, ids, blk));
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    MOE_TIMED_LAUNCH(MOE_KERNEL_DISPATCH_SCAN, s,
-                     dispatch_scan_kernel<<<1, 1024, 0, s>>>(nblk, E, capacity, blk, counts, kept, offsets));
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    MOE_TIMED_LAUNCH(MOE_KERNEL_DISPATCH_SCATTER, s,
-                     dispatch_scatter_kernel<<<nblk, kWave, (size_t)E * 4, s>>>(
-                         n, E, nbits, ch, capacity, ids, blk, offsets, assign_row, row_assign));
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipError_t err;
+    if (n <= DS_SMALL_MAX) {
+        MOE_TIMED_LAUNCH(MOE_KERNEL_DISPATCH_SCATTER, s,
+                         dispatch_small_kernel<<<1, 1024, 0, s>>>(n, E, nbits, capacity, ids, counts,
+                                                                  kept, offsets, assign_row, row_assign));
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    } else {
+        MOE_TIMED_LAUNCH(MOE_KERNEL_DISPATCH_COUNT, s,
+                         dispatch_count_kernel<<<nblk, DS_THREADS, (size_t)E * 4, s>>>(n, E, ch, ids, blk));
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        MOE_TIMED_LAUNCH(MOE_KERNEL_DISPATCH_SCAN, s,
+                         dispatch_scan_kernel<<<1, 1024, 0, s>>>(nblk, E, capacity, blk, counts, kept, offsets));
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        MOE_TIMED_LAUNCH(MOE_KERNEL_DISPATCH_SCATTER, s,
+                         dispatch_scatter_kernel<<<nblk, kWave, (size_t)E * 4, s>>>(
+                             n, E, nbits, ch, capacity, ids, blk, offsets, assign_row, row_assign));
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     if (x == nullptr) return hipSuccess;
     const int esz = dtype == MOE_DTYPE_F32 ? 4 : 2;
     const int rows_per_block = DS_THREADS / kWave;

@@ -5,14 +5,18 @@
 //
 // Each workgroup owns a strip of 16 weight rows of one expert (for gate/up the
 // same 16 rows of W1 and of W3) and its four waves split the reduction
-// dimension.  A wave streams its rows in 128-wide k chunks: lane (r, g) loads 64
-// contiguous bytes of row r (so the four lanes of a row read 256 contiguous
-// bytes), and feeds them to four 16x16x32 MFMAs whose k positions are permuted
-// identically for the weight and the token operand.  The expert's tokens (at
-// most 32 per pass, two 16-column MFMA blocks) are the second operand, read
-// from L2.  Partial sums meet in LDS, where the fixed-order sum and the epilogue
-// (SiLU(g1) * g3 for gate/up) run.  Experts with no rows are skipped without
-// touching their weights.
+// dimension.  A wave streams its rows in chunks of 128 * CPI k values.  In a
+// chunk, load instruction s reads bytes [64 s, 64 s + 64) of the chunk of every
+// row: the four lanes of a row read 64 contiguous bytes, and the 4 * CPI
+// instructions cover the chunk.  The k positions fed to the 16x16x32 MFMAs
+// follow the same permutation for the weight and for the token operand, so the
+// contraction is unchanged.  Weights are read once with plain loads (on gfx950
+// the non-temporal hint measured slower for this stream) and double-buffered
+// in registers.  The expert's tokens (the second operand, 16 * NCB per pass;
+// an expert with more rows takes several passes over its weights) are read
+// from L2 just before their use.  Partial sums meet in LDS, where the
+// fixed-order sum and the epilogue (SiLU(g1) * g3 for gate/up) run.  Experts
+// with no rows are skipped without touching their weights.
 #include "../device_common.h"
 #include "../launch.h"
 
@@ -21,86 +25,127 @@ namespace moe {
 constexpr int DC_ROWS = 16;
 constexpr int DC_WAVES = 4;
 constexpr int DC_KCH = 128;
-constexpr int DC_MAXCB = 2;
 
-template <bool GATED>
+// 16 bytes at row[k .. k+8) when k < K, else zeros.  The load itself is
+// unconditional (at a clamped, valid address) and the zeros come from a
+// select, so the compiler emits no branch around it and can keep exact
+// counts of the loads in flight.  K is a positive multiple of 8.
+__device__ __forceinline__ u32x4 load16_masked(const bf16* row, int k, int K) {
+    const u32x4 v = *(const u32x4*)(row + min(k, K - 8));
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    return k < K ? v : z;
+}
+
+template <bool GATED, int CPI, int NCB, bool ALIGNED>
 __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
     int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ offsets,
     const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
     constexpr int NG = GATED ? 2 : 1;
-    __shared__ float red[DC_WAVES][DC_MAXCB][NG][4][kWave];
+    constexpr int NS = 4 * CPI;          // 32-wide slices per chunk
+    constexpr int KCH = DC_KCH * CPI;  // k per chunk
+    __shared__ float red[DC_WAVES - 1][NCB][NG][4][kWave];
     const int e = blockIdx.y;
     const int n0 = blockIdx.x * DC_ROWS;
     const int r0 = offsets[e];
     const int m = min(offsets[e + 1], n_rows) - r0;
     if (r0 < 0 || m <= 0) return;
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid & (kWave - 1);
     const int rl = lane & 15;
     const int g = lane >> 4;
-    const int nch = (K + DC_KCH - 1) / DC_KCH;
+    const int nch = (K + KCH - 1) / KCH;
     const int per = (nch + DC_WAVES - 1) / DC_WAVES;
-    const int c_beg = wave * per;
+    const int c_beg = min(nch, wave * per);
     const int c_end = min(nch, c_beg + per);
     const int wrow = min(n0 + rl, N - 1);
     const bf16* wa = Wa + ((size_t)e * N + wrow) * K;
     const bf16* wb = GATED ? Wb + ((size_t)e * N + wrow) * K : nullptr;
+    const int kl = g * 8;  // this lane's k offset inside each 32-wide slice
 
-    for (int p0 = 0; p0 < m; p0 += 16 * DC_MAXCB) {
-        const int mp = min(m - p0, 16 * DC_MAXCB);
+    for (int p0 = 0; p0 < m; p0 += 16 * NCB) {
+        const int mp = min(m - p0, 16 * NCB);
         const int ncb = (mp + 15) / 16;
-        f32x4 acc[DC_MAXCB][NG];
+        f32x4 acc[NCB][NG];
 #pragma unroll
-        for (int cb = 0; cb < DC_MAXCB; ++cb)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) acc[cb][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16* arow[DC_MAXCB];
+        const bf16* arow[NCB];
 #pragma unroll
-        for (int cb = 0; cb < DC_MAXCB; ++cb)
+        for (int cb = 0; cb < NCB; ++cb)
             arow[cb] = A + (size_t)(r0 + p0 + min(cb * 16 + rl, mp - 1)) * K;
 
-        for (int c = c_beg; c < c_end; ++c) {
-            const int kb = c * DC_KCH + g * 32;
-            u32x4 wv[4];
-            u32x4 wv3[4];
+        // Double buffer in registers: the weight loads of chunk c + 1 are issued
+        // after the token loads of chunk c, so waiting for the tokens of chunk c
+        // (and the weights of chunk c, issued one step earlier) leaves chunk
+        // c + 1 in flight while chunk c is multiplied.
+        u32x4 wc[NG][NS], wn[NG][NS];
+        auto load_w = [&](int c, u32x4 (&wd)[NG][NS]) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = kb + s * 8;
-                wv[s] = load16_or_zero(wa + k, k < K);
-                if (GATED) wv3[s] = load16_or_zero(wb + k, k < K);
+            for (int s = 0; s < NS; ++s) {
+                const int k = c * KCH + s * 32 + kl;
+                if (ALIGNED) {  // K is a multiple of the chunk: every load is in range
+                    wd[0][s] = load16(wa + k);
+                    if (GATED) wd[NG - 1][s] = load16(wb + k);
+                } else {
+                    wd[0][s] = load16_masked(wa, k, K);
+                    if (GATED) wd[NG - 1][s] = load16_masked(wb, k, K);
+                }
             }
+        };
+        if (c_beg < c_end) load_w(c_beg, wc);
+        for (int c = c_beg; c < c_end; ++c) {
+            u32x4 xv[NCB][NS];
 #pragma unroll
-            for (int cb = 0; cb < DC_MAXCB; ++cb) {
-                if (cb < ncb) {
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (NCB == 1 || cb < ncb) {
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int k = kb + s * 8;
-                        const bf16x8 xv = as_bf16x8(load16_or_zero(arow[cb] + k, k < K));
-                        acc[cb][0] = mfma16(as_bf16x8(wv[s]), xv, acc[cb][0]);
-                        if (GATED) acc[cb][NG - 1] = mfma16(as_bf16x8(wv3[s]), xv, acc[cb][NG - 1]);
+                    for (int s = 0; s < NS; ++s) {
+                        const int k = c * KCH + s * 32 + kl;
+                        xv[cb][s] = ALIGNED ? load16(arow[cb] + k) : load16_masked(arow[cb], k, K);
                     }
                 }
             }
-        }
+            if (c + 1 < c_end) load_w(c + 1, wn);
 #pragma unroll
-        for (int cb = 0; cb < DC_MAXCB; ++cb)
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (NCB == 1 || cb < ncb) {
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) {
+                        const bf16x8 xb = as_bf16x8(xv[cb][s]);
+                        acc[cb][0] = mfma16(as_bf16x8(wc[0][s]), xb, acc[cb][0]);
+                        if (GATED) acc[cb][NG - 1] = mfma16(as_bf16x8(wc[NG - 1][s]), xb, acc[cb][NG - 1]);
+                    }
+                }
+            }
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) red[wave][cb][gi][i][lane] = acc[cb][gi][i];
+                for (int s = 0; s < NS; ++s) wc[gi][s] = wn[gi][s];
+        }
+        if (wave > 0) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) red[wave - 1][cb][gi][i][lane] = acc[cb][gi][i];
+        }
         __syncthreads();
         if (wave == 0) {
-            for (int cb = 0; cb < ncb; ++cb) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (cb >= ncb) break;
                 // lane holds output (weight row 4g + i, token column rl) of this block
                 const int tcol = cb * 16 + rl;
                 float v[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float s0 = red[0][cb][0][i][lane];
-                    float s1 = GATED ? red[0][cb][NG - 1][i][lane] : 0.0f;
+                    float s0 = acc[cb][0][i];
+                    float s1 = GATED ? acc[cb][NG - 1][i] : 0.0f;
 #pragma unroll
-                    for (int w = 1; w < DC_WAVES; ++w) {
+                    for (int w = 0; w < DC_WAVES - 1; ++w) {
                         s0 += red[w][cb][0][i][lane];
                         if (GATED) s1 += red[w][cb][NG - 1][i][lane];
                     }
@@ -123,21 +168,30 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
     }
 }
 
-hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* x_perm, const int32_t* offsets,
-                             const void* w1, const void* w3, const void* w2, void* act, void* h,
-                             hipStream_t s) {
+template <bool ALIGNED>
+static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* x_perm,
+                                  const int32_t* offsets, const void* w1, const void* w3,
+                                  const void* w2, void* act, void* h, hipStream_t s) {
     dim3 g1((F + DC_ROWS - 1) / DC_ROWS, E);
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_GATE_UP, s,
-                     ffn_decode_kernel<true><<<g1, DC_WAVES * kWave, 0, s>>>(
+                     ffn_decode_kernel<true, 1, 1, ALIGNED><<<g1, DC_WAVES * kWave, 0, s>>>(
                          n_rows, F, d, (const bf16*)x_perm, offsets, (const bf16*)w1, (const bf16*)w3,
                          (bf16*)act));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     dim3 g2((d + DC_ROWS - 1) / DC_ROWS, E);
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
-                     ffn_decode_kernel<false><<<g2, DC_WAVES * kWave, 0, s>>>(
+                     ffn_decode_kernel<false, 1, 1, ALIGNED><<<g2, DC_WAVES * kWave, 0, s>>>(
                          n_rows, d, F, (const bf16*)act, offsets, (const bf16*)w2, nullptr, (bf16*)h));
     return hipGetLastError();
+}
+
+hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* x_perm, const int32_t* offsets,
+                             const void* w1, const void* w3, const void* w2, void* act, void* h,
+                             hipStream_t s) {
+    if (d % DC_KCH == 0 && F % DC_KCH == 0)
+        return launch_decode_t<true>(n_rows, E, d, F, x_perm, offsets, w1, w3, w2, act, h, s);
+    return launch_decode_t<false>(n_rows, E, d, F, x_perm, offsets, w1, w3, w2, act, h, s);
 }
 
 }  // namespace moe

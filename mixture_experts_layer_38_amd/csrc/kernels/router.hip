@@ -3,12 +3,21 @@
 // MoE notes (www.cf-1.com/news/5905749) §1.2 and §2 steps 1-3; MoE inference
 // engineering page (ybb.press/quantum-computing/18594) §1 and §1.2.
 //
-// bf16 path: one fused kernel.  A workgroup owns 32 tokens; W_r is staged
-// through LDS in 64-row slices, transposed to [expert][k] so that each MFMA
-// operand is one 16-byte LDS read; x is read straight from HBM with 16-byte
-// loads.  The 32 x E logit tile then stays in LDS for the routing phase, where
-// each wave routes one token at a time (lanes own experts lane, lane+64, ...).
-// fp32 path: a plain FMA kernel for the scores, then the same routing phase.
+// bf16 path, three kernels:
+//   transpose : W_r [d, E] -> W_r^T [E, d] in the workspace, so that both MFMA
+//               operands are contiguous along d;
+//   gemm      : logits as a batched matmul over all tokens (§2.1 of the notes):
+//               each wave owns 16 tokens x 16*NEB experts over one slice of d
+//               and streams its token rows from HBM with 16x16x32 bf16 MFMAs
+//               (the next 128-wide chunk of x is in flight while the current
+//               one is multiplied; W_r^T comes from L2).  Small token counts
+//               split d over the grid so that enough waves stream x; the
+//               per-slice partial scores go to the workspace;
+//   route     : one wave per token sums the slices in slice order (a fixed
+//               order, so the logits are deterministic), adds the bias, and
+//               runs the softmax, the top-K and the renormalisation with lanes
+//               owning experts lane, lane + 64, ...
+// fp32 path: a plain FMA kernel for the scores, then the same route kernel.
 #include <math.h>
 
 #include "../device_common.h"
@@ -16,15 +25,16 @@
 
 namespace moe {
 
-constexpr int RT_BT = 32;            // tokens per workgroup
-constexpr int RT_KC = 64;            // rows of W_r staged per step
-constexpr int RT_LDSK = RT_KC + 8;   // padded LDS row of the transposed W_r slice (bf16)
+constexpr int RT_BT = 8;  // tokens per route workgroup (two per wave)
 constexpr int RT_THREADS = 256;
+constexpr int RG_KCH = 128;  // d chunk per gemm iteration
 
-// Route one token whose E logits are `lg`; the wave computes it together.
-// psum[j] accumulates this wave's probabilities of expert lane + 64 j.
+// ---- route ---------------------------------------------------------------------
+// Route one token whose biased-or-not scores this lane holds for experts
+// lane + 64 j.  The wave computes it together.  psum[j] accumulates this
+// wave's probabilities of expert lane + 64 j.
 template <int MAXV>
-__device__ __forceinline__ void route_token(const float* lg, int E, int K, const float* bias,
+__device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int K, const float* bias,
                                             float* probs_row, int32_t* ids_row, float* w_row,
                                             float (&psum)[MAXV]) {
     const int lane = lane_id();
@@ -35,7 +45,7 @@ __device__ __forceinline__ void route_token(const float* lg, int E, int K, const
         const int e = lane + j * kWave;
         if (e < E) {
             const float b = bias ? bias[e] : 0.0f;
-            v[j] = lg[e] + b;  // one fp32 addition, round to nearest even
+            v[j] = lg[j] + b;  // one fp32 addition, round to nearest even
             m = fmaxf(m, v[j]);
         } else {
             v[j] = -INFINITY;
@@ -104,26 +114,48 @@ __device__ __forceinline__ void route_token(const float* lg, int E, int K, const
     }
 }
 
-// Routing phase shared by the kernels: tokens t0 .. t0+RT_BT-1, logits of
-// token t at lg + (t - t0) * lg_stride.  Writes the per-block prob sums.
+// src holds nsplit slices [nsplit][T][E] of partial scores (nsplit = 1: the
+// scores themselves).  When logits_out is given, the summed scores are written
+// there.  psum_part (optional) receives this block's per-expert probability sums.
 template <int MAXV>
-__device__ void route_block(int T, int E, int K, int t0, const float* lg, int lg_stride,
-                            const float* bias, float* probs, int32_t* ids, float* w,
-                            float* psum_part, float* red /* LDS, 4*E floats */) {
+__global__ __launch_bounds__(RT_THREADS) void route_kernel(
+    int T, int E, int K, int nsplit, const float* __restrict__ src, float* __restrict__ logits_out,
+    const float* __restrict__ bias, float* __restrict__ probs, float* __restrict__ psum_part,
+    int32_t* __restrict__ ids, float* __restrict__ w) {
+    extern __shared__ float red[];  // [RT_THREADS / kWave][E]
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
     float psum[MAXV];
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) psum[j] = 0.0f;
+    const size_t slice = (size_t)T * E;
     for (int tt = wave; tt < RT_BT; tt += RT_THREADS / kWave) {
-        const int t = t0 + tt;
+        const int t = blockIdx.x * RT_BT + tt;
         if (t >= T) break;
-        route_token<MAXV>(lg + (size_t)tt * lg_stride, E, K, bias,
-                          probs ? probs + (size_t)t * E : nullptr, ids + (size_t)t * K,
-                          w + (size_t)t * K, psum);
+        float lg[MAXV];
+#pragma unroll
+        for (int j = 0; j < MAXV; ++j) {
+            const int e = lane + j * kWave;
+            float acc = 0.0f;
+            if (e < E) {
+                // slices in ascending order; loads issued eight at a time
+                const float* p = src + (size_t)t * E + e;
+                for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+                    float v8[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) v8[q] = sp0 + q < nsplit ? p[(size_t)(sp0 + q) * slice] : 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (sp0 + q < nsplit) acc = (sp0 + q == 0) ? v8[q] : acc + v8[q];
+                }
+                if (logits_out) logits_out[(size_t)t * E + e] = acc;
+            }
+            lg[j] = acc;
+        }
+        route_token<MAXV>(lg, E, K, bias, probs ? probs + (size_t)t * E : nullptr,
+                          ids + (size_t)t * K, w + (size_t)t * K, psum);
     }
     if (psum_part) {
-        __syncthreads();  // red may alias the logit tile
 #pragma unroll
         for (int j = 0; j < MAXV; ++j) {
             const int e = lane + j * kWave;
@@ -138,105 +170,116 @@ __device__ void route_block(int T, int E, int K, int t0, const float* lg, int lg
     }
 }
 
-template <int MAXV>
-__global__ __launch_bounds__(RT_THREADS) void router_bf16_kernel(
-    int T, int d, int E, int K, int ep_max, const bf16* __restrict__ x,
-    const bf16* __restrict__ wr, const float* __restrict__ bias, float* __restrict__ logits,
-    float* __restrict__ probs, float* __restrict__ psum_part, int32_t* __restrict__ ids,
-    float* __restrict__ w) {
-    extern __shared__ __align__(16) char smem[];
-    float* lg = reinterpret_cast<float*>(smem);                                  // [RT_BT][E]
-    bf16* wt = reinterpret_cast<bf16*>(smem + ((RT_BT * E * 4 + 15) & ~15));  // [ep_max][RT_LDSK]
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave;
-    const int lane = tid & (kWave - 1);
-    const int t0 = blockIdx.x * RT_BT;
-    const int mb = wave & 1;      // 16-token block of this wave
-    const int npar = wave >> 1;   // this wave takes expert blocks npar, npar + 2, ...
-    const int tok = min(t0 + mb * 16 + (lane & 15), T - 1);
-    const bf16* xrow = x + (size_t)tok * d;
-    const int kq = (lane >> 4) * 8;
-    const bool vec_ok = (E % 8) == 0;
-
-    for (int e0 = 0; e0 < E; e0 += ep_max) {
-        const int ep = min(ep_max, E - e0);
-        const int nblk = (ep + 15) / 16;
-        f32x4 acc[8];
+// prob_sum[e] = sum over route blocks of the per-block sums: one wave per
+// expert, lane j takes blocks j, j + 64, ... in double, then a fixed butterfly.
+__global__ __launch_bounds__(256) void psum_reduce_kernel(int nblk, int E,
+                                                         const float* __restrict__ part,
+                                                         float* __restrict__ prob_sum) {
+    const int e = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
+    if (e >= E) return;
+    const int lane = lane_id();
+    double s = 0.0;
+    for (int b = lane; b < nblk; b += kWave) s += (double)part[(size_t)b * E + e];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int k0 = 0; k0 < d; k0 += RT_KC) {
-            __syncthreads();
-            // Stage W_r[k0 .. k0+RT_KC) x [e0 .. e0+ep) as wt[e][k].
-            if (vec_ok) {
-                const int nv = RT_KC * (ep / 8);
-                for (int v = tid; v < nv; v += RT_THREADS) {
-                    const int kk = v / (ep / 8);
-                    const int ee = (v - kk * (ep / 8)) * 8;
-                    u32x4 val = load16_or_zero(wr + (size_t)(k0 + kk) * E + e0 + ee, k0 + kk < d);
-                    const bf16x8 b = as_bf16x8(val);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) wt[(ee + i) * RT_LDSK + kk] = b[i];
-                }
-            } else {
-                const int ne = RT_KC * ep;
-                for (int v = tid; v < ne; v += RT_THREADS) {
-                    const int kk = v / ep;
-                    const int ee = v - kk * ep;
-                    wt[ee * RT_LDSK + kk] = (k0 + kk < d) ? wr[(size_t)(k0 + kk) * E + e0 + ee] : (bf16)0.0f;
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int ks = 0; ks < RT_KC; ks += 32) {
-                const int k = k0 + ks + kq;
-                const bf16x8 a = as_bf16x8(load16_or_zero(xrow + k, k < d));
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int nb = npar + 2 * j;
-                    if (nb < nblk) {
-                        int er = nb * 16 + (lane & 15);
-                        er = er < ep ? er : ep - 1;
-                        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&wt[er * RT_LDSK + ks + kq]);
-                        acc[j] = mfma16(a, b, acc[j]);
-                    }
-                }
-            }
-        }
-        // acc[j][i] = logit of token (lane/16)*4 + i of this wave's block, expert nb*16 + lane%16
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int nb = npar + 2 * j;
-            if (nb < nblk) {
-                const int e = e0 + nb * 16 + (lane & 15);
-                if (e < e0 + ep) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tt = mb * 16 + (lane >> 4) * 4 + i;
-                        const int t = t0 + tt;
-                        lg[tt * E + e] = acc[j][i];
-                        if (t < T) logits[(size_t)t * E + e] = acc[j][i];
-                    }
-                }
-            }
-        }
-    }
-    __syncthreads();
-    // psum reduction reuses the W_r staging area (4 * E floats fit in it).
-    route_block<MAXV>(T, E, K, t0, lg, E, bias, probs, ids, w, psum_part,
-                      reinterpret_cast<float*>(wt));
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) prob_sum[e] = (float)s;
 }
 
-// Routing of given fp32 logits (no GEMM): the x == NULL mode and the fp32 path.
-template <int MAXV>
-__global__ __launch_bounds__(RT_THREADS) void route_logits_kernel(
-    int T, int E, int K, const float* __restrict__ logits, const float* __restrict__ bias,
-    float* __restrict__ probs, float* __restrict__ psum_part, int32_t* __restrict__ ids,
-    float* __restrict__ w) {
-    extern __shared__ __align__(16) char smem[];
-    const int t0 = blockIdx.x * RT_BT;
-    route_block<MAXV>(T, E, K, t0, logits + (size_t)t0 * E, E, bias, probs, ids, w, psum_part,
-                      reinterpret_cast<float*>(smem));
+// ---- scores ---------------------------------------------------------------------
+// W_r [d, E] -> W_r^T [E, d] through a padded LDS tile.
+__global__ __launch_bounds__(256) void router_transpose_kernel(int d, int E, const bf16* __restrict__ wr,
+                                                              bf16* __restrict__ wrt) {
+    __shared__ bf16 tile[64][65];
+    const int k0 = blockIdx.x * 64;
+    const int e0 = blockIdx.y * 64;
+    bf16 v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {  // all sixteen loads in flight together
+        const int i = threadIdx.x + q * 256;
+        const int kk = i / 64, ee = i % 64;
+        v[q] = (k0 + kk < d && e0 + ee < E) ? wr[(size_t)(k0 + kk) * E + e0 + ee] : (bf16)0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int i = threadIdx.x + q * 256;
+        tile[i / 64][i % 64] = v[q];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int ee = i / 64, kk = i % 64;
+        if (k0 + kk < d && e0 + ee < E) wrt[(size_t)(e0 + ee) * d + k0 + kk] = tile[kk][ee];
+    }
+}
+
+// out[split][t][e] = sum over d in this split's slice of x[t][k] * W_r^T[e][k].
+// Wave tile: 16 tokens x 16*NEB experts; lane (r = lane % 16, g = lane / 16).
+// In each 32-wide slice of a 128-wide chunk the four lanes of a row read 64
+// contiguous bytes; both operands use the same k order.
+template <int NEB>
+__global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, int kspan,
+                                                         const bf16* __restrict__ x,
+                                                         const bf16* __restrict__ wrt,
+                                                         float* __restrict__ out) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int lane = lane_id();
+    const int rl = lane & 15;
+    const int g = lane >> 4;
+    const int tb = blockIdx.x * 4 + wave;
+    if (tb * 16 >= T) return;  // no barrier in this kernel
+    const int eb0 = blockIdx.y * 16 * NEB;
+    const int k_beg = blockIdx.z * kspan;
+    const int k_end = min(d, k_beg + kspan);
+    const int kl = g * 8;
+    const bf16* xr = x + (size_t)min(tb * 16 + rl, T - 1) * d + kl;
+    const bf16* wrow[NEB];
+#pragma unroll
+    for (int j = 0; j < NEB; ++j) wrow[j] = wrt + (size_t)min(eb0 + j * 16 + rl, E - 1) * d + kl;
+    f32x4 acc[NEB];
+#pragma unroll
+    for (int j = 0; j < NEB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nch = (k_end - k_beg + RG_KCH - 1) / RG_KCH;
+    u32x4 xc[4], xn[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int k = k_beg + s * 32;
+        xc[s] = load16_or_zero(xr + k, k + kl < k_end);
+    }
+    for (int c = 0; c < nch; ++c) {
+        const int kc = k_beg + c * RG_KCH;
+        u32x4 wv[NEB][4];
+#pragma unroll
+        for (int j = 0; j < NEB; ++j)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int k = kc + s * 32;
+                wv[j][s] = load16_or_zero(wrow[j] + k, k + kl < k_end);
+            }
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int k = kc + RG_KCH + s * 32;
+                xn[s] = load16_or_zero(xr + k, k + kl < k_end);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NEB; ++j) acc[j] = mfma16(as_bf16x8(xc[s]), as_bf16x8(wv[j][s]), acc[j]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xc[s] = xn[s];
+    }
+    // acc[j][i]: token tb*16 + 4g + i, expert eb0 + 16 j + rl
+    float* o = out + (size_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int j = 0; j < NEB; ++j) {
+        const int e = eb0 + j * 16 + rl;
+        if (e >= E) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = tb * 16 + g * 4 + i;
+            if (t < T) o[(size_t)t * E + e] = acc[j][i];
+        }
+    }
 }
 
 // fp32 scores: one thread per (token, expert), plain FMA over d.
@@ -254,80 +297,119 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(int T, int d, in
     logits[i] = s;
 }
 
-// prob_sum[e] = sum over blocks (ascending) of the per-block sums, in double.
-__global__ __launch_bounds__(256) void psum_reduce_kernel(int nblk, int E,
-                                                         const float* __restrict__ part,
-                                                         float* __restrict__ prob_sum) {
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= E) return;
-    double s = 0.0;
-    for (int b = 0; b < nblk; ++b) s += (double)part[(size_t)b * E + e];
-    prob_sum[e] = (float)s;
+// ---- host side ------------------------------------------------------------------
+static int router_neb(int E) {
+    if (E <= 16) return 1;
+    if (E <= 32) return 2;
+    if (E <= 64) return 4;
+    return 8;
+}
+
+// Slices of d for the score GEMM: enough waves to stream x, each slice a
+// multiple of the chunk width, and at most 8 MB of partial scores.
+static int router_splits(int T, int d, int E) {
+    const int neb = router_neb(E);
+    const long waves = (long)((T + 15) / 16) * ((E + 16 * neb - 1) / (16 * neb));
+    const int max_split = max(1, d / RG_KCH);
+    int ns = 1;
+    while (ns * 2 <= max_split && waves * ns < 4096 &&
+           (size_t)(ns * 2) * T * E * sizeof(float) <= ((size_t)8 << 20))
+        ns *= 2;
+    return ns;
+}
+
+static int router_kspan(int d, int ns) {
+    const int chunks = (d + RG_KCH - 1) / RG_KCH;
+    return (chunks + ns - 1) / ns * RG_KCH;
 }
 
 int router_num_blocks(int T, int /*dtype*/) { return (T + RT_BT - 1) / RT_BT; }
 
-size_t router_ws_bytes(int T, int E, int dtype) {
-    return align_up((size_t)router_num_blocks(T, dtype) * E * sizeof(float), 256);
+// Workspace: [W_r^T (bf16 with x)] [partial scores (bf16 with x, > 1 slice)] [prob-sum partials]
+struct RouterLayout {
+    size_t wrt, part, psum, total;
+    int ns;
+};
+
+static RouterLayout router_layout(int T, int d, int E, int dtype) {
+    RouterLayout L;
+    size_t o = 0;
+    L.ns = dtype == MOE_DTYPE_BF16 ? router_splits(T, d, E) : 1;
+    L.wrt = o;
+    if (dtype == MOE_DTYPE_BF16) o += align_up((size_t)E * d * 2, 256);
+    L.part = o;
+    if (L.ns > 1) o += align_up((size_t)L.ns * T * E * sizeof(float), 256);
+    L.psum = o;
+    o += align_up((size_t)router_num_blocks(T, dtype) * E * sizeof(float), 256);
+    L.total = o;
+    return L;
 }
 
-static int route_ep_max(int E) { return E > 512 ? 128 : 256; }
-
-static size_t router_lds_bytes(int E) {
-    const size_t lg = (RT_BT * (size_t)E * 4 + 15) / 16 * 16;
-    size_t wt = (size_t)route_ep_max(E) * RT_LDSK * 2;
-    const size_t red = (size_t)4 * E * 4;
-    if (wt < red) wt = red;
-    return lg + wt;
-}
+size_t router_ws_bytes(int T, int d, int E, int dtype) { return router_layout(T, d, E, dtype).total; }
 
 template <int MAXV>
-static hipError_t launch_router_t(int T, int d, int E, int K, int dtype, const void* x,
-                                  const void* wr, const float* bias, float* logits, float* probs,
-                                  float* psum_part, int32_t* ids, float* w, hipStream_t s) {
-    const int nblk = router_num_blocks(T, dtype);
-    if (x != nullptr && dtype == MOE_DTYPE_BF16) {
-        const size_t lds = router_lds_bytes(E);
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t err = hipFuncSetAttribute((const void*)router_bf16_kernel<MAXV>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 160 * 1024);
-            if (err != hipSuccess) return err;
-            attr_set = true;
-        }
-        MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER, s,
-                         router_bf16_kernel<MAXV><<<nblk, RT_THREADS, lds, s>>>(
-                             T, d, E, K, route_ep_max(E), (const bf16*)x, (const bf16*)wr, bias,
-                             logits, probs, psum_part, ids, w));
-        return hipGetLastError();
-    }
-    if (x != nullptr) {  // fp32 scores first
-        const size_t n = (size_t)T * E;
-        router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-            T, d, E, (const float*)x, (const float*)wr, logits);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
+static hipError_t launch_route_t(int T, int E, int K, int nsplit, const float* src, float* logits_out,
+                                 const float* bias, float* probs, float* psum_part, int32_t* ids,
+                                 float* w, hipStream_t s) {
+    const int nblk = router_num_blocks(T, 0);
     MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER, s,
-                     route_logits_kernel<MAXV><<<nblk, RT_THREADS, (size_t)4 * E * 4, s>>>(
-                         T, E, K, logits, bias, probs, psum_part, ids, w));
+                     route_kernel<MAXV><<<nblk, RT_THREADS, (size_t)(RT_THREADS / kWave) * E * 4, s>>>(
+                         T, E, K, nsplit, src, logits_out, bias, probs, psum_part, ids, w));
     return hipGetLastError();
+}
+
+static hipError_t launch_route(int T, int E, int K, int nsplit, const float* src, float* logits_out,
+                               const float* bias, float* probs, float* psum_part, int32_t* ids,
+                               float* w, hipStream_t s) {
+    if (E <= 64) return launch_route_t<1>(T, E, K, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
+    if (E <= 256) return launch_route_t<4>(T, E, K, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
+    return launch_route_t<16>(T, E, K, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
+}
+
+template <int NEB>
+static void launch_gemm_t(int T, int d, int E, int ns, const bf16* x, const bf16* wrt, float* out,
+                          hipStream_t s) {
+    dim3 grid((unsigned)((T + 63) / 64), (unsigned)((E + 16 * NEB - 1) / (16 * NEB)), (unsigned)ns);
+    router_gemm_kernel<NEB><<<grid, 256, 0, s>>>(T, d, E, router_kspan(d, ns), x, wrt, out);
 }
 
 hipError_t launch_router(int T, int d, int E, int K, int dtype, const void* x,
                          const void* w_router, const float* bias, float* logits, float* probs,
                          float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s) {
-    float* part = prob_sum ? reinterpret_cast<float*>(ws) : nullptr;
+    const RouterLayout L = router_layout(T, d, E, dtype);
+    char* base = reinterpret_cast<char*>(ws);
+    float* part = prob_sum ? reinterpret_cast<float*>(base + L.psum) : nullptr;
     hipError_t err;
-    if (E <= 64)
-        err = launch_router_t<1>(T, d, E, K, dtype, x, w_router, bias, logits, probs, part, ids, w, s);
-    else if (E <= 256)
-        err = launch_router_t<4>(T, d, E, K, dtype, x, w_router, bias, logits, probs, part, ids, w, s);
-    else
-        err = launch_router_t<16>(T, d, E, K, dtype, x, w_router, bias, logits, probs, part, ids, w, s);
+    int nsplit = 1;
+    const float* src = logits;
+    float* logits_out = nullptr;
+    if (x != nullptr && dtype == MOE_DTYPE_BF16) {
+        bf16* wrt = reinterpret_cast<bf16*>(base + L.wrt);
+        dim3 tg((unsigned)((d + 63) / 64), (unsigned)((E + 63) / 64));
+        router_transpose_kernel<<<tg, 256, 0, s>>>(d, E, (const bf16*)w_router, wrt);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        nsplit = L.ns;
+        float* gout = nsplit > 1 ? reinterpret_cast<float*>(base + L.part) : logits;
+        switch (router_neb(E)) {
+            case 1: launch_gemm_t<1>(T, d, E, nsplit, (const bf16*)x, wrt, gout, s); break;
+            case 2: launch_gemm_t<2>(T, d, E, nsplit, (const bf16*)x, wrt, gout, s); break;
+            case 4: launch_gemm_t<4>(T, d, E, nsplit, (const bf16*)x, wrt, gout, s); break;
+            default: launch_gemm_t<8>(T, d, E, nsplit, (const bf16*)x, wrt, gout, s); break;
+        }
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if (nsplit > 1) {
+            src = gout;
+            logits_out = logits;
+        }
+    } else if (x != nullptr) {  // fp32 scores
+        const size_t n = (size_t)T * E;
+        router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+            T, d, E, (const float*)x, (const float*)w_router, logits);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    err = launch_route(T, E, K, nsplit, src, logits_out, bias, probs, part, ids, w, s);
     if (err != hipSuccess || !prob_sum) return err;
-    psum_reduce_kernel<<<(E + 255) / 256, 256, 0, s>>>(router_num_blocks(T, dtype), E, part, prob_sum);
+    psum_reduce_kernel<<<(E + 3) / 4, 256, 0, s>>>(router_num_blocks(T, dtype), E, part, prob_sum);
     return hipGetLastError();
 }
 

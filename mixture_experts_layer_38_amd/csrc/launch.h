@@ -25,9 +25,11 @@ void timer_after(int kid, hipStream_t s);
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---- router ----------------------------------------------------------------
-// Number of token blocks the router uses (its prob_sum partials are per block).
+// Number of token blocks of the route kernel (its prob_sum partials are per block).
 int router_num_blocks(int T, int dtype);
-size_t router_ws_bytes(int T, int E, int dtype);
+// Workspace of the router: W_r^T and partial scores (bf16 scores from x) and
+// the per-block probability sums.
+size_t router_ws_bytes(int T, int d, int E, int dtype);
 hipError_t launch_router(int T, int d, int E, int K, int dtype, const void* x,
                          const void* w_router, const float* bias, float* logits, float* probs,
                          float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s);

@@ -91,7 +91,7 @@ static ForwardLayout forward_layout(const moe_problem* p) {
     L.x_perm = take(n * d * es);
     L.act = take(n * F * es);
     L.h = take(n * d * es);
-    L.route_ws = take(router_ws_bytes(p->T, p->n_experts, p->dtype));
+    L.route_ws = take(router_ws_bytes(p->T, p->d_model, p->n_experts, p->dtype));
     L.disp_ws = take(dispatch_ws_bytes(p->T, p->top_k, p->n_experts));
     L.ffn_ws = take(ffn_ws_bytes(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype));
     L.total = o;
@@ -146,7 +146,7 @@ moe_status moe_route_workspace_size(const moe_problem* p, size_t* bytes) {
     moe_status st = check_problem(p);
     if (st != MOE_OK) return st;
     if (!bytes) return MOE_ERR_INVALID_ARG;
-    *bytes = router_ws_bytes(p->T, p->n_experts, p->dtype);
+    *bytes = router_ws_bytes(p->T, p->d_model, p->n_experts, p->dtype);
     return MOE_OK;
 }
 
@@ -187,8 +187,9 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
     OPTIONAL(logit_bias);
     OPTIONAL(probs);
     OPTIONAL(prob_sum);
-    if (prob_sum) {
-        if (!ws || ws_bytes < router_ws_bytes(p->T, p->n_experts, p->dtype)) return MOE_ERR_WORKSPACE;
+    if (prob_sum || (x && p->dtype == MOE_DTYPE_BF16)) {
+        if (!ws || ws_bytes < router_ws_bytes(p->T, p->d_model, p->n_experts, p->dtype))
+            return MOE_ERR_WORKSPACE;
         if (!aligned16(ws)) return MOE_ERR_ALIGNMENT;
     }
     return hip_status(launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype, x,
