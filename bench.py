@@ -30,25 +30,34 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 
 
-def kernel_source_hash() -> str:
+# Source files whose text fixes each timed kernel (a change invalidates its counters).
+KERNEL_SOURCES = {
+    "decode": ["mixture_experts_layer_38_amd/csrc/kernels/ffn_decode.hip",
+               "mixture_experts_layer_38_amd/csrc/device_common.h"],
+    "prefill": ["mixture_experts_layer_38_amd/csrc/kernels/ffn_prefill.hip",
+                "mixture_experts_layer_38_amd/csrc/device_common.h"],
+}
+
+
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    kdir = os.path.join(ROOT, "mixture_experts_layer_38_amd", "csrc", "kernels")
-    for f in sorted(os.listdir(kdir)):
-        if f.startswith("ffn"):
-            with open(os.path.join(kdir, f), "rb") as fh:
-                h.update(fh.read())
+    for rel in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel sources (else None)."""
+def load_traffic(workload: str, kernel: str, family: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the same counters on a
+    plain copy of known size; None when the summary is missing or was taken on
+    other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != kernel_source_hash():
+    if rec.get("kernel_source_sha") != kernel_source_hash(family):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -105,19 +114,29 @@ def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str):
     return wall, float(np.mean(kern_ms)) if kern_ms else float("nan"), counts, kept
 
 
-def cpu_baseline(cfg, inp, n_tokens: int):
+def cpu_baseline(cfg, inp, min_seconds: float = 10.0, max_reps: int = 200):
+    """The CPU oracle (fp64, OpenMP on this host's cores) on the same workload:
+    whole forward passes of the first min(T, 32) tokens (routing, grouping,
+    SwiGLU experts and combine), repeated until at least `min_seconds` of CPU
+    work have been timed."""
     import oracle
     orc = oracle.get()
+    n_tokens = min(cfg.T, 32)
     toks = np.arange(n_tokens, dtype=np.int64)
     x = np.ascontiguousarray(inp["x"][:n_tokens])
+    reps = 0
     t0 = time.perf_counter()
-    orc.forward(x, inp["w_router"], inp["w1"], inp["w3"], inp["w2"], cfg.K,
-                inp["logit_bias"], cfg.capacity, toks)
-    dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": orc.num_threads(),
+    while True:
+        orc.forward(x, inp["w_router"], inp["w1"], inp["w3"], inp["w2"], cfg.K,
+                    inp["logit_bias"], cfg.capacity, toks)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
+    return {"value": reps * n_tokens / dt, "unit": "tokens/s", "cores": orc.num_threads(),
             "kind": "oracle", "seconds": dt,
-            "sample": f"{n_tokens} tokens of {cfg.name} (full routing, grouping and "
-                      f"fp64 SwiGLU experts + combine for every sampled token)"}
+            "sample": f"{reps} full forward passes of {n_tokens} tokens of {cfg.name} "
+                      f"(router, routing, grouping, fp64 SwiGLU experts and combine)"}
 
 
 def main():
@@ -155,7 +174,7 @@ def main():
     gb, gf = gate_up_algorithmic(cfg, kept)
     lb, lf = layer_algorithmic(cfg, kept)
     achieved = gb / (k_ms * 1e-3) / 1e9
-    traffic = load_traffic(cfg.name, "ffn_gate_up")
+    traffic = load_traffic(cfg.name, "ffn_gate_up", "decode" if cfg.T <= 64 else "prefill")
     result = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
@@ -190,14 +209,14 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "ffn_gate_up",
                          "achieved": pgf / (pk_ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": pgf / (pk_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
-                         "traffic": load_traffic(pcfg.name, "ffn_gate_up"), "kernel_ms": pk_ms},
+                         "traffic": load_traffic(pcfg.name, "ffn_gate_up", "prefill"), "kernel_ms": pk_ms},
             "layer_mfma_frac": plf / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
             "counts": pcounts.tolist(),
         }
         del player, px
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, min(cfg.T, 32))
+        result["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(result), flush=True)
 
 

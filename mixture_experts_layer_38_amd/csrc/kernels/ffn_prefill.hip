@@ -6,29 +6,55 @@
 //
 // Both GEMMs are "rows x weights^T" with both operands contiguous along the
 // reduction dimension: act = SiLU(X W1^T) * (X W3^T) and h = act W2^T.
-// A device-side plan (one tiny kernel) cuts every expert's rows into 128-row
-// tiles; the GEMM grid is (weight tiles) x (an upper bound on row tiles), and
-// workgroups past the real tile count exit at once.  A workgroup computes a
-// 128 x 128 output tile with four waves in a 2 x 2 grid, each wave 64 x 64 with
-// 32x32x16 bf16 MFMAs (weights as the first operand so each lane ends up with
-// four consecutive output columns of one token).  Operand tiles move HBM ->
-// registers -> LDS (padded rows, double buffered, one barrier per 64-wide k
-// step).  For gate/up the weight tile interleaves 32-row blocks of W1 and W3 of
-// the same output columns, so the SiLU-gate epilogue is local to each wave.
+//
+// Tiles.  A device-side plan (one tiny kernel) cuts every expert's rows into
+// 256-row tiles.  An output tile is 256 token rows x 256 weight rows; for
+// gate/up the 256 weight rows are 128 features of W1 and the same 128 of W3,
+// interleaved in 32-row blocks so that the SiLU-gate epilogue stays inside
+// each wave.  Eight waves split the tile as 4 (tokens, 64 each) x 2 (weights,
+// 128 each); a wave owns 4 x 2 blocks of 32x32 accumulated with
+// v_mfma_f32_32x32x16_bf16 (weights as the first operand, so that each lane
+// ends with four consecutive output columns of one token).
+//
+// Pipeline (K a multiple of 128).  Operand tiles are 32 wide in k and go
+// straight from HBM/L2 into LDS with global_load_lds_dwordx4 (no staging
+// registers): a ring of four stages (128 KB, one workgroup per CU) keeps three
+// stages in flight while one is multiplied, with one barrier per stage.  Tile
+// rows are 64 bytes; row r keeps its 16-byte chunk c in slot c ^ swz(r), so
+// the fragment reads of 32 consecutive rows are free of bank conflicts (the
+// global addresses carry the permutation, since the DMA writes lanes in
+// order).  Other K use a generic variant further down.
+//
+// Order.  Workgroup b runs on XCD b % 8.  The tiles are listed expert by
+// expert in groups of PF_GM row tiles (row tile fastest inside a group), and
+// XCD x takes the x-th contiguous eighth of that list, so the tiles that run
+// together on one XCD share their token rows and weight rows in its L2.
 #include "../device_common.h"
 #include "../launch.h"
 
 namespace moe {
 
-constexpr int PF_BM = 128;
-constexpr int PF_BN = 128;
-constexpr int PF_BK = 64;
-constexpr int PF_LDS = PF_BK + 8;  // padded LDS row length (bf16)
-constexpr int PF_THREADS = 256;
+constexpr int PF_BM = 256;          // token rows per tile
+constexpr int PF_BN = 256;          // weight rows per tile
+constexpr int PF_BK = 32;           // k per pipeline stage
+constexpr int PF_NST = 4;           // LDS stages in the ring
+constexpr int PF_THREADS = 512;
+constexpr int PF_GM = 4;            // row tiles per group in the tile order
+constexpr int PF_XCD = 8;
+constexpr int PF_STAGE = PF_BM * PF_BK;  // bf16 elements of one operand stage (PF_BM == PF_BN)
+
+// Swizzle of the four 16-byte chunks of a 64-byte tile row: row r keeps
+// chunk c in slot c ^ pf_swz(r), so the fragment reads of 32 consecutive
+// rows (one chunk each) fall in distinct banks.
+__device__ __forceinline__ int pf_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt immediate: vmcnt <= n, no wait on the other counters.
+#define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
 
 int prefill_max_mtiles(int n_rows, int E) { return n_rows / PF_BM + E + 1; }
 
-// One block; thread e cuts expert e's rows into PF_BM-row tiles.
+// One block; thread e cuts expert e's rows into PF_BM-row tiles: *mt_count
+// row tiles, tile j of expert mt_expert[j] starting at grouped row mt_row0[j].
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt,
                                                        const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ mt_count,
@@ -60,103 +86,133 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt,
     if (e == E - 1) *mt_count = min(start + nt, max_mt);
 }
 
+// N: weight rows of one expert (gate/up: F, down: d); K: reduction length,
+// a multiple of PF_BK * PF_NST; n_nt: weight tiles per row tile.
 template <bool GATED>
 __global__ __launch_bounds__(PF_THREADS) void ffn_prefill_kernel(
-    int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ mt_count,
-    const int32_t* __restrict__ mt_expert, const int32_t* __restrict__ mt_row0,
-    const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
-    bf16* __restrict__ out) {
-    const int mt = blockIdx.y;
-    if (mt >= *mt_count) return;
+    int n_rows, int N, int K, int n_nt, const bf16* __restrict__ A,
+    const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
+    const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ offsets,
+    const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
+    __shared__ __align__(1024) bf16 sA0[PF_STAGE], sA1[PF_STAGE], sA2[PF_STAGE], sA3[PF_STAGE];
+    __shared__ __align__(1024) bf16 sB0[PF_STAGE], sB1[PF_STAGE], sB2[PF_STAGE], sB3[PF_STAGE];
+    const int n_mt = *mt_count;
+    const int tiles = n_mt * n_nt;
+    const int per_xcd = (tiles + PF_XCD - 1) / PF_XCD;
+    const int slot = blockIdx.x / PF_XCD;
+    if (slot >= per_xcd) return;
+    const int t = (blockIdx.x % PF_XCD) * per_xcd + slot;
+    if (t >= tiles) return;
+    const int grp = t / (PF_GM * n_nt);
+    const int first = grp * PF_GM;
+    const int gsize = min(PF_GM, n_mt - first);
+    const int rem = t - grp * PF_GM * n_nt;
+    const int mt = first + rem % gsize;
+    const int nt = rem / gsize;
     const int e = mt_expert[mt];
     const int row0 = mt_row0[mt];
     const int row_end = min(offsets[e + 1], n_rows);
-    const int nt = blockIdx.x;
 
-    __shared__ __align__(16) bf16 sA[2][PF_BM * PF_LDS];
-    __shared__ __align__(16) bf16 sB[2][PF_BN * PF_LDS];
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int lane = lane_id();
 
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave;
-    const int lane = tid & (kWave - 1);
-    const int lr = tid >> 3;        // 0..31: row within a 32-row slab
-    const int lc = (tid & 7) * 8;   // 16-byte chunk within the 64-wide k step
-
-    const bf16* a_src[4];
-    const bf16* b_src[4];
+    // Loads: a stage is 16 A and 16 B wave instructions of 16 rows x 64 bytes;
+    // wave w issues A rows [16 w, +16) and [16 (w + 8), +16), and the same B
+    // rows.  Lane p fills slot p % 4 of tile row p / 4 of its instruction,
+    // fetching the chunk that the swizzle puts there.
+    const int lr = lane >> 2;
+    const int ls = lane & 3;
+    const bf16* a_src[2];
+    const bf16* b_src[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = min(row0 + lr + 32 * j, n_rows - 1);
-        a_src[j] = A + (size_t)r * K + lc;
-        const int br = lr + 32 * j;
+    for (int j = 0; j < 2; ++j) {
+        const int tr = 16 * (wave + 8 * j) + lr;  // tile row, A and B alike
+        const int c = ls ^ pf_swz(tr);
+        const int r = min(row0 + tr, n_rows - 1);
+        a_src[j] = A + (size_t)r * K + c * 8;
         if (GATED) {
-            const int blk = br >> 5;
-            const int f = min(nt * 64 + (blk >> 1) * 32 + (br & 31), N - 1);
+            // tile rows [128 w, 128 w + 128) = W1, W3, W1, W3 blocks of 32 rows
+            // for features nt*128 + 64 w + [0, 64)
+            const int w = tr >> 7;
+            const int blk = (tr >> 5) & 3;
+            const int f = min(nt * 128 + w * 64 + (blk >> 1) * 32 + (tr & 31), N - 1);
             const bf16* W = (blk & 1) ? Wb : Wa;
-            b_src[j] = W + ((size_t)e * N + f) * K + lc;
+            b_src[j] = W + ((size_t)e * N + f) * K + c * 8;
         } else {
-            const int nr = min(nt * PF_BN + br, N - 1);
-            b_src[j] = Wa + ((size_t)e * N + nr) * K + lc;
+            const int nr = min(nt * PF_BN + tr, N - 1);
+            b_src[j] = Wa + ((size_t)e * N + nr) * K + c * 8;
         }
     }
-
-    const int nk = (K + PF_BK - 1) / PF_BK;
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int kt) {
-        const bool ok = kt * PF_BK + lc < K;
+    const int nk = K / PF_BK;
+    auto issue = [&](int kt, bf16* dA, bf16* dB) {
+        const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ra[j] = load16_or_zero(a_src[j] + (size_t)kt * PF_BK, ok);
-            rb[j] = load16_or_zero(b_src[j] + (size_t)kt * PF_BK, ok);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            store16(&sA[buf][(lr + 32 * j) * PF_LDS + lc], ra[j]);
-            store16(&sB[buf][(lr + 32 * j) * PF_LDS + lc], rb[j]);
+        for (int j = 0; j < 2; ++j) {
+            const int off = 16 * (wave + 8 * j) * PF_BK;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[j] + ko),
+                                             (__attribute__((address_space(3))) void*)(dA + off), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b_src[j] + ko),
+                                             (__attribute__((address_space(3))) void*)(dB + off), 16, 0, 0);
         }
     };
 
-    const int wm = wave & 1;   // token half of the tile
-    const int wn = wave >> 1;  // weight half of the tile
-    f32x16 acc[2][2];
+    const int wm = wave & 3;   // token block of 64
+    const int wn = wave >> 2;  // weight block of 128
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+    // Fragment of row r (r % 32 == lane % 32), 16-byte chunk c: element offset.
+    const int fsw = pf_swz(lane & 31);
+    const int fhalf = lane >> 5;
+    auto frag = [&](const bf16* buf, int row, int ks) {
+        const int c = (2 * ks + fhalf) ^ fsw;
+        return *reinterpret_cast<const bf16x8*>(&buf[row * PF_BK + c * 8]);
+    };
+    auto compute = [&](const bf16* cA, const bf16* cB) {
 #pragma unroll
-        for (int ks = 0; ks < PF_BK; ks += 16) {
-            const int koff = ks + (lane >> 5) * 8;
-            bf16x8 fw[2], ft[2];
+        for (int ks = 0; ks < PF_BK / 16; ++ks) {
+            bf16x8 fw[4], ft[2];
 #pragma unroll
-            for (int wb = 0; wb < 2; ++wb)
-                fw[wb] = *reinterpret_cast<const bf16x8*>(
-                    &sB[cur][(wn * 64 + wb * 32 + (lane & 31)) * PF_LDS + koff]);
+            for (int wb = 0; wb < 4; ++wb) fw[wb] = frag(cB, wn * 128 + wb * 32 + (lane & 31), ks);
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-                ft[tb] = *reinterpret_cast<const bf16x8*>(
-                    &sA[cur][(wm * 64 + tb * 32 + (lane & 31)) * PF_LDS + koff]);
+            for (int tb = 0; tb < 2; ++tb) ft[tb] = frag(cA, wm * 64 + tb * 32 + (lane & 31), ks);
 #pragma unroll
-            for (int wb = 0; wb < 2; ++wb)
+            for (int wb = 0; wb < 4; ++wb)
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) acc[wb][tb] = mfma32(fw[wb], ft[tb], acc[wb][tb]);
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
-        __syncthreads();
+    };
+    // Stage kt is read from ring slot kt % 4.  Before it is read, this wave's
+    // loads of stage kt are done (the 8 loads of the next two stages may still
+    // be in flight) and a barrier makes every wave's loads of it visible; the
+    // same barrier tells every wave that slot (kt + 3) % 4 = (kt - 1) % 4 has
+    // been read, so the loads of stage kt + 3 go there.  Every step issues its
+    // four loads (clamped to the last stage at the end), so the count of loads
+    // in flight is the same on every path.
+    auto step = [&](int kt, const bf16* cA, const bf16* cB, bf16* nA, bf16* nB) {
+        PF_WAIT_VM(8);
+        __builtin_amdgcn_s_barrier();
+        issue(kt + 3, nA, nB);
+        compute(cA, cB);
+    };
+    issue(0, sA0, sB0);
+    issue(1, sA1, sB1);
+    issue(2, sA2, sB2);
+    for (int k0 = 0; k0 < nk; k0 += PF_NST) {
+        step(k0, sA0, sB0, sA3, sB3);
+        step(k0 + 1, sA1, sB1, sA0, sB0);
+        step(k0 + 2, sA2, sB2, sA1, sB1);
+        step(k0 + 3, sA3, sB3, sA2, sB2);
     }
+    PF_WAIT_VM(0);
 
     // acc[wb][tb][i]: weight row 8*(i/4) + 4*(lane/32) + i%4 of block wb,
-    // token (lane % 32) of block tb.
+    // token lane % 32 of block tb.
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         const int grow = row0 + wm * 64 + tb * 32 + (lane & 31);
@@ -166,21 +222,196 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_prefill_kernel(
         for (int q = 0; q < 4; ++q) {
             const int wr = 8 * q + 4 * (lane >> 5);
             if (GATED) {
-                const int f = nt * 64 + wn * 32 + wr;
-                float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = silu(acc[0][tb][4 * q + r]) * acc[1][tb][4 * q + r];
-                if (f + 3 < N) {
-                    bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-                    *reinterpret_cast<bf16x4*>(orow + f) = pk;
-                } else {
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int f = nt * 128 + wn * 64 + pr * 32 + wr;
+                    float v[4];
+#pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (f + r < N) orow[f + r] = (bf16)v[r];
+                        v[r] = silu(acc[2 * pr][tb][4 * q + r]) * acc[2 * pr + 1][tb][4 * q + r];
+                    if (f + 3 < N) {
+                        bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+                        *reinterpret_cast<bf16x4*>(orow + f) = pk;
+                    } else {
+                        for (int r = 0; r < 4; ++r)
+                            if (f + r < N) orow[f + r] = (bf16)v[r];
+                    }
                 }
             } else {
 #pragma unroll
-                for (int wb = 0; wb < 2; ++wb) {
-                    const int c = nt * PF_BN + wn * 64 + wb * 32 + wr;
+                for (int wb = 0; wb < 4; ++wb) {
+                    const int c = nt * PF_BN + wn * 128 + wb * 32 + wr;
+                    const f32x16& a = acc[wb][tb];
+                    if (c + 3 < N) {
+                        bf16x4 pk = {(bf16)a[4 * q], (bf16)a[4 * q + 1], (bf16)a[4 * q + 2],
+                                     (bf16)a[4 * q + 3]};
+                        *reinterpret_cast<bf16x4*>(orow + c) = pk;
+                    } else {
+                        for (int r = 0; r < 4; ++r)
+                            if (c + r < N) orow[c + r] = (bf16)a[4 * q + r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---- generic variant (any K) ---------------------------------------------------
+constexpr int PG_BM = 256;
+constexpr int PG_BN = 256;
+constexpr int PG_BK = 64;
+constexpr int PG_LDS = PG_BK + 8;  // padded LDS row (bf16 elements)
+constexpr int PG_THREADS = 512;
+constexpr int PG_GM = PF_GM;
+constexpr int PG_XCD = PF_XCD;
+constexpr size_t PG_TILE_ELEMS = (size_t)PG_BM * PG_LDS;
+constexpr size_t PG_LDS_BYTES = 4 * PG_TILE_ELEMS * sizeof(bf16);
+
+// Generic variant for any K (a multiple of 8): the same tiles, with operands
+// staged HBM/L2 -> registers -> LDS (rows padded to 144 bytes), double
+// buffered with one 64-wide k step in flight.  N, K, n_nt as above.
+template <bool GATED>
+__global__ __launch_bounds__(PG_THREADS) void ffn_prefill_generic_kernel(
+    int n_rows, int N, int K, int n_nt, const bf16* __restrict__ A,
+    const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
+    const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ offsets,
+    const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
+    extern __shared__ __align__(16) bf16 smem[];
+    const int n_mt = *mt_count;
+    const int tiles = n_mt * n_nt;
+    const int per_xcd = (tiles + PG_XCD - 1) / PG_XCD;
+    const int slot = blockIdx.x / PG_XCD;
+    if (slot >= per_xcd) return;
+    const int t = (blockIdx.x % PG_XCD) * per_xcd + slot;
+    if (t >= tiles) return;
+    const int grp = t / (PG_GM * n_nt);
+    const int first = grp * PG_GM;
+    const int gsize = min(PG_GM, n_mt - first);
+    const int rem = t - grp * PG_GM * n_nt;
+    const int mt = first + rem % gsize;
+    const int nt = rem / gsize;
+    const int e = mt_expert[mt];
+    const int row0 = mt_row0[mt];
+    const int row_end = min(offsets[e + 1], n_rows);
+
+    bf16* sA = smem;                      // [2][PG_BM][PG_LDS]
+    bf16* sB = smem + 2 * PG_TILE_ELEMS;  // [2][PG_BN][PG_LDS]
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid & (kWave - 1);
+    const int lr = tid >> 3;        // 0..63: row within a 64-row slab
+    const int lc = (tid & 7) * 8;   // 16-byte chunk within the 64-wide k step
+
+    const bf16* a_src[4];
+    const bf16* b_src[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = min(row0 + lr + 64 * j, n_rows - 1);
+        a_src[j] = A + (size_t)r * K + lc;
+        const int br = lr + 64 * j;  // weight row inside the tile
+        if (GATED) {
+            // tile rows [128 w, 128 w + 128) = W1, W3, W1, W3 blocks of 32 rows
+            // for features nt*128 + 64 w + [0, 64)
+            const int w = br >> 7;
+            const int blk = (br >> 5) & 3;
+            const int f = min(nt * 128 + w * 64 + (blk >> 1) * 32 + (br & 31), N - 1);
+            const bf16* W = (blk & 1) ? Wb : Wa;
+            b_src[j] = W + ((size_t)e * N + f) * K + lc;
+        } else {
+            const int nr = min(nt * PG_BN + br, N - 1);
+            b_src[j] = Wa + ((size_t)e * N + nr) * K + lc;
+        }
+    }
+
+    const int nk = (K + PG_BK - 1) / PG_BK;
+    u32x4 ra[4], rb[4];
+    auto gload = [&](int kt) {
+        const bool ok = kt * PG_BK + lc < K;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ra[j] = load16_or_zero(a_src[j] + (size_t)kt * PG_BK, ok);
+            rb[j] = load16_or_zero(b_src[j] + (size_t)kt * PG_BK, ok);
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            store16(&sA[buf * PG_TILE_ELEMS + (lr + 64 * j) * PG_LDS + lc], ra[j]);
+            store16(&sB[buf * PG_TILE_ELEMS + (lr + 64 * j) * PG_LDS + lc], rb[j]);
+        }
+    };
+
+    const int wm = wave & 3;   // token block of 64
+    const int wn = wave >> 2;  // weight block of 128
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 8;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        const bf16* cA = sA + cur * PG_TILE_ELEMS;
+        const bf16* cB = sB + cur * PG_TILE_ELEMS;
+#pragma unroll
+        for (int ks = 0; ks < PG_BK; ks += 16) {
+            bf16x8 fw[4], ft[2];
+#pragma unroll
+            for (int wb = 0; wb < 4; ++wb)
+                fw[wb] = *reinterpret_cast<const bf16x8*>(
+                    &cB[(wn * 128 + wb * 32 + frag_row) * PG_LDS + ks + frag_k]);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+                ft[tb] = *reinterpret_cast<const bf16x8*>(
+                    &cA[(wm * 64 + tb * 32 + frag_row) * PG_LDS + ks + frag_k]);
+#pragma unroll
+            for (int wb = 0; wb < 4; ++wb)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) acc[wb][tb] = mfma32(fw[wb], ft[tb], acc[wb][tb]);
+        }
+        if (kt + 1 < nk) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // acc[wb][tb][i]: weight row 8*(i/4) + 4*(lane/32) + i%4 of block wb,
+    // token lane % 32 of block tb.
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int grow = row0 + wm * 64 + tb * 32 + (lane & 31);
+        if (grow >= row_end) continue;
+        bf16* orow = out + (size_t)grow * N;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int wr = 8 * q + 4 * (lane >> 5);
+            if (GATED) {
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int f = nt * 128 + wn * 64 + pr * 32 + wr;
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = silu(acc[2 * pr][tb][4 * q + r]) * acc[2 * pr + 1][tb][4 * q + r];
+                    if (f + 3 < N) {
+                        bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+                        *reinterpret_cast<bf16x4*>(orow + f) = pk;
+                    } else {
+                        for (int r = 0; r < 4; ++r)
+                            if (f + r < N) orow[f + r] = (bf16)v[r];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int wb = 0; wb < 4; ++wb) {
+                    const int c = nt * PG_BN + wn * 128 + wb * 32 + wr;
                     const f32x16& a = acc[wb][tb];
                     if (c + 3 < N) {
                         bf16x4 pk = {(bf16)a[4 * q], (bf16)a[4 * q + 1], (bf16)a[4 * q + 2],
@@ -200,6 +431,35 @@ size_t prefill_ws_bytes(int n_rows, int E) {
     return align_up((size_t)(1 + 2 * prefill_max_mtiles(n_rows, E)) * sizeof(int32_t), 256);
 }
 
+template <bool GATED>
+static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int max_mt,
+                                      const bf16* A, const int32_t* mt_count,
+                                      const int32_t* mt_expert, const int32_t* mt_row0,
+                                      const int32_t* offsets, const bf16* Wa, const bf16* Wb,
+                                      bf16* out, hipStream_t s) {
+    const long tiles = (long)max_mt * n_nt;
+    const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
+    const int kid = GATED ? MOE_KERNEL_FFN_GATE_UP : MOE_KERNEL_FFN_DOWN;
+    if (K % (PF_BK * PF_NST) == 0) {
+        MOE_TIMED_LAUNCH(kid, s,
+                         ffn_prefill_kernel<GATED><<<grid, PF_THREADS, 0, s>>>(
+                             n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out));
+        return hipGetLastError();
+    }
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute((const void*)ffn_prefill_generic_kernel<GATED>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)PG_LDS_BYTES);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
+    MOE_TIMED_LAUNCH(kid, s,
+                     ffn_prefill_generic_kernel<GATED><<<grid, PG_THREADS, PG_LDS_BYTES, s>>>(
+                         n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out));
+    return hipGetLastError();
+}
+
 hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* x_perm,
                               const int32_t* offsets, const void* w1, const void* w3,
                               const void* w2, void* act, void* h, void* ws, hipStream_t s) {
@@ -211,18 +471,13 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* x_per
                      ffn_plan_kernel<<<1, 1024, 0, s>>>(E, max_mt, offsets, mt_count, mt_expert, mt_row0));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    dim3 g1((F + 63) / 64, max_mt);
-    MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_GATE_UP, s,
-                     ffn_prefill_kernel<true><<<g1, PF_THREADS, 0, s>>>(
-                         n_rows, F, d, (const bf16*)x_perm, mt_count, mt_expert, mt_row0, offsets,
-                         (const bf16*)w1, (const bf16*)w3, (bf16*)act));
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    dim3 g2((d + PF_BN - 1) / PF_BN, max_mt);
-    MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
-                     ffn_prefill_kernel<false><<<g2, PF_THREADS, 0, s>>>(
-                         n_rows, d, F, (const bf16*)act, mt_count, mt_expert, mt_row0, offsets,
-                         (const bf16*)w2, nullptr, (bf16*)h));
-    return hipGetLastError();
+    err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, (const bf16*)x_perm,
+                                    mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
+                                    (const bf16*)w3, (bf16*)act, s);
+    if (err != hipSuccess) return err;
+    return launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt,
+                                      (const bf16*)act, mt_count, mt_expert, mt_row0, offsets,
+                                      (const bf16*)w2, nullptr, (bf16*)h, s);
 }
 
 }  // namespace moe

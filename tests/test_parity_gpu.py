@@ -22,6 +22,7 @@ REDUCED = {
     "decode_d512": scaled(C["mixtral_decode"], d=512, F=1536),
     "prefill_t600_ragged": scaled(C["mixtral_prefill"], T=600, d=264, F=200),
     "prefill_t2048": scaled(C["mixtral_prefill"], T=2048, d=512, F=1024),
+    "prefill_t700_ntail": scaled(C["mixtral_prefill"], T=700, d=384, F=640),
     "dsv3_t256": scaled(C["dsv3_routed"], T=256, d=256, F=256),
     "capacity_t2048": scaled(C["capacity_top2"], T=2048, d=256, F=1408),
     "fp32_ragged": scaled(C["tiny_fp32"], T=77, d=40, E=5, K=3, F=24),
