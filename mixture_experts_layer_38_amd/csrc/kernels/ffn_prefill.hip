@@ -11,19 +11,20 @@
 // 256-row tiles.  An output tile is 256 token rows x 256 weight rows; for
 // gate/up the 256 weight rows are 128 features of W1 and the same 128 of W3,
 // interleaved in 32-row blocks so that the SiLU-gate epilogue stays inside
-// each wave.  Eight waves split the tile as 4 (tokens, 64 each) x 2 (weights,
-// 128 each); a wave owns 4 x 2 blocks of 32x32 accumulated with
+// each wave.  Four waves (one per SIMD) split the tile 2 x 2; a wave owns
+// 128 x 128 as 4 x 4 blocks of 32x32 accumulated in AGPRs with
 // v_mfma_f32_32x32x16_bf16 (weights as the first operand, so that each lane
 // ends with four consecutive output columns of one token).
 //
-// Pipeline (K a multiple of 128).  Operand tiles are 32 wide in k and go
-// straight from HBM/L2 into LDS with global_load_lds_dwordx4 (no staging
-// registers): a ring of four stages (128 KB, one workgroup per CU) keeps three
-// stages in flight while one is multiplied, with one barrier per stage.  Tile
-// rows are 64 bytes; row r keeps its 16-byte chunk c in slot c ^ swz(r), so
-// the fragment reads of 32 consecutive rows are free of bank conflicts (the
-// global addresses carry the permutation, since the DMA writes lanes in
-// order).  Other K use a generic variant further down.
+// Pipeline (K a multiple of 64).  Operand stages are 64 wide in k, so a tile
+// row is one 128-byte line, and go straight from HBM/L2 into LDS with
+// global_load_lds_dwordx4 (no staging registers): two 64 KB slots, the next
+// stage in flight while the current one is multiplied, one barrier per stage.
+// Row r keeps its 16-byte chunk c in slot c ^ swz(r), so the fragment reads
+// of consecutive rows are free of bank conflicts (the global addresses carry
+// the permutation, since the DMA writes lanes in order).  Inside a stage the
+// LDS reads of each 16-wide k quarter are interleaved with the MFMAs of the
+// quarter before.  Other K use a generic variant further down.
 //
 // Order.  Workgroup b runs on XCD b % 8.  The tiles are listed expert by
 // expert in groups of PF_GM row tiles (row tile fastest inside a group), and
@@ -36,20 +37,21 @@ namespace moe {
 
 constexpr int PF_BM = 256;          // token rows per tile
 constexpr int PF_BN = 256;          // weight rows per tile
-constexpr int PF_BK = 32;           // k per pipeline stage
-constexpr int PF_NST = 4;           // LDS stages in the ring
-constexpr int PF_THREADS = 512;
-constexpr int PF_GM = 4;            // row tiles per group in the tile order
+constexpr int PF_BK = 64;           // k per pipeline stage (128-byte tile rows)
+constexpr int PF_THREADS = 256;
+constexpr int PF_GM = 8;            // row tiles per group in the tile order
 constexpr int PF_XCD = 8;
 constexpr int PF_STAGE = PF_BM * PF_BK;  // bf16 elements of one operand stage (PF_BM == PF_BN)
 
-// Swizzle of the four 16-byte chunks of a 64-byte tile row: row r keeps
-// chunk c in slot c ^ pf_swz(r), so the fragment reads of 32 consecutive
-// rows (one chunk each) fall in distinct banks.
-__device__ __forceinline__ int pf_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Swizzle of the eight 16-byte chunks of a 128-byte tile row: row r keeps
+// chunk c in slot c ^ pf_swz(r), so fragment reads of consecutive rows (one
+// chunk each) fall in distinct banks.
+__device__ __forceinline__ int pf_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // s_waitcnt immediate: vmcnt <= n, no wait on the other counters.
 #define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+// s_waitcnt immediate: lgkmcnt == 0, no wait on the other counters.
+#define PF_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
 
 int prefill_max_mtiles(int n_rows, int E) { return n_rows / PF_BM + E + 1; }
 
@@ -87,15 +89,16 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt,
 }
 
 // N: weight rows of one expert (gate/up: F, down: d); K: reduction length,
-// a multiple of PF_BK * PF_NST; n_nt: weight tiles per row tile.
+// a multiple of PF_BK; n_nt: weight tiles per row tile.
 template <bool GATED>
-__global__ __launch_bounds__(PF_THREADS) void ffn_prefill_kernel(
+__global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_prefill_kernel(
     int n_rows, int N, int K, int n_nt, const bf16* __restrict__ A,
     const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
     const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ offsets,
     const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
-    __shared__ __align__(1024) bf16 sA0[PF_STAGE], sA1[PF_STAGE], sA2[PF_STAGE], sA3[PF_STAGE];
-    __shared__ __align__(1024) bf16 sB0[PF_STAGE], sB1[PF_STAGE], sB2[PF_STAGE], sB3[PF_STAGE];
+    __shared__ __align__(1024) bf16 sA0[PF_STAGE], sA1[PF_STAGE];
+    __shared__ __align__(1024) bf16 sB0[PF_STAGE], sB1[PF_STAGE];
     const int n_mt = *mt_count;
     const int tiles = n_mt * n_nt;
     const int per_xcd = (tiles + PF_XCD - 1) / PF_XCD;
@@ -116,17 +119,17 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_prefill_kernel(
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int lane = lane_id();
 
-    // Loads: a stage is 16 A and 16 B wave instructions of 16 rows x 64 bytes;
-    // wave w issues A rows [16 w, +16) and [16 (w + 8), +16), and the same B
-    // rows.  Lane p fills slot p % 4 of tile row p / 4 of its instruction,
+    // Loads: a stage is 32 A and 32 B wave instructions of 8 rows x 128 bytes;
+    // wave w issues A rows [8 (w + 4 j), +8) for j = 0..7, and the same B
+    // rows.  Lane p fills slot p % 8 of tile row p / 8 of its instruction,
     // fetching the chunk that the swizzle puts there.
-    const int lr = lane >> 2;
-    const int ls = lane & 3;
-    const bf16* a_src[2];
-    const bf16* b_src[2];
+    const int lr = lane >> 3;
+    const int ls = lane & 7;
+    const bf16* a_src[8];
+    const bf16* b_src[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int tr = 16 * (wave + 8 * j) + lr;  // tile row, A and B alike
+    for (int j = 0; j < 8; ++j) {
+        const int tr = 8 * (wave + 4 * j) + lr;  // tile row, A and B alike
         const int c = ls ^ pf_swz(tr);
         const int r = min(row0 + tr, n_rows - 1);
         a_src[j] = A + (size_t)r * K + c * 8;
@@ -147,8 +150,8 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_prefill_kernel(
     auto issue = [&](int kt, bf16* dA, bf16* dB) {
         const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int off = 16 * (wave + 8 * j) * PF_BK;
+        for (int j = 0; j < 8; ++j) {
+            const int off = 8 * (wave + 4 * j) * PF_BK;
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[j] + ko),
                                              (__attribute__((address_space(3))) void*)(dA + off), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b_src[j] + ko),
@@ -156,66 +159,110 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_prefill_kernel(
         }
     };
 
-    const int wm = wave & 3;   // token block of 64
-    const int wn = wave >> 2;  // weight block of 128
-    f32x16 acc[4][2];
+    const int wm = wave & 1;   // token block of 128
+    const int wn = wave >> 1;  // weight block of 128
+    f32x16 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-    // Fragment of row r (r % 32 == lane % 32), 16-byte chunk c: element offset.
-    const int fsw = pf_swz(lane & 31);
+    // Fragment rows: weight rows wn*128 + 32 wb + lane%32, token rows
+    // wm*128 + 32 tb + lane%32; their swizzles are fixed for the whole tile.
     const int fhalf = lane >> 5;
-    auto frag = [&](const bf16* buf, int row, int ks) {
-        const int c = (2 * ks + fhalf) ^ fsw;
-        return *reinterpret_cast<const bf16x8*>(&buf[row * PF_BK + c * 8]);
+    int wsw[4], tsw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        wsw[i] = pf_swz(wn * 128 + i * 32 + (lane & 31));
+        tsw[i] = pf_swz(wm * 128 + i * 32 + (lane & 31));
+    }
+    struct Frags {
+        bf16x8 w[4], t[4];
     };
-    auto compute = [&](const bf16* cA, const bf16* cB) {
+    // 16-wide k quarter q of a stage: chunk 2q + (lane / 32).
+    auto read = [&](const bf16* cA, const bf16* cB, int q, Frags& f) {
+        const int c = 2 * q + fhalf;
 #pragma unroll
-        for (int ks = 0; ks < PF_BK / 16; ++ks) {
-            bf16x8 fw[4], ft[2];
+        for (int wb = 0; wb < 4; ++wb)
+            f.w[wb] = *reinterpret_cast<const bf16x8*>(
+                &cB[(wn * 128 + wb * 32 + (lane & 31)) * PF_BK + (c ^ wsw[wb]) * 8]);
 #pragma unroll
-            for (int wb = 0; wb < 4; ++wb) fw[wb] = frag(cB, wn * 128 + wb * 32 + (lane & 31), ks);
+        for (int tb = 0; tb < 4; ++tb)
+            f.t[tb] = *reinterpret_cast<const bf16x8*>(
+                &cA[(wm * 128 + tb * 32 + (lane & 31)) * PF_BK + (c ^ tsw[tb]) * 8]);
+    };
+    auto mma = [&](const Frags& f) {
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) ft[tb] = frag(cA, wm * 64 + tb * 32 + (lane & 31), ks);
+        for (int wb = 0; wb < 4; ++wb)
 #pragma unroll
-            for (int wb = 0; wb < 4; ++wb)
+            for (int tb = 0; tb < 4; ++tb) acc[wb][tb] = mfma32(f.w[wb], f.t[tb], acc[wb][tb]);
+    };
+    // Interleave: one MFMA, then one LDS fragment read, eight times, then the
+    // remaining eight MFMAs (the reads issue in the shadow of the MFMAs).
+    auto interleave = [&]() {
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) acc[wb][tb] = mfma32(fw[wb], ft[tb], acc[wb][tb]);
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
-    // Stage kt is read from ring slot kt % 4.  Before it is read, this wave's
-    // loads of stage kt are done (the 8 loads of the next two stages may still
-    // be in flight) and a barrier makes every wave's loads of it visible; the
-    // same barrier tells every wave that slot (kt + 3) % 4 = (kt - 1) % 4 has
-    // been read, so the loads of stage kt + 3 go there.  Every step issues its
-    // four loads (clamped to the last stage at the end), so the count of loads
-    // in flight is the same on every path.
-    auto step = [&](int kt, const bf16* cA, const bf16* cB, bf16* nA, bf16* nB) {
-        PF_WAIT_VM(8);
+    // Stage kt lives in slot kt % 2 and is multiplied in four 16-wide
+    // quarters; the LDS reads of each quarter overlap the MFMAs of the quarter
+    // before.  After the third quarter's MFMAs: wait until this wave's reads
+    // of slot kt % 2 are done and its loads of stage kt + 1 have landed; a
+    // barrier then makes stage kt + 1 visible to every wave and tells every
+    // wave that slot kt % 2 is free, and the loads of stage kt + 2 go there;
+    // the first quarter of stage kt + 1 is read during the last quarter's
+    // MFMAs.  Every step issues the same loads and reads (clamped to the last
+    // stage at the end, into a slot no later step reads), so the counts of
+    // loads in flight are the same on every path.
+    Frags fa, fb;
+    auto step = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB) {
+        read(cA, cB, 1, fb);
+        mma(fa);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        read(cA, cB, 2, fa);
+        mma(fb);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        read(cA, cB, 3, fb);
+        mma(fa);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        PF_WAIT_LGKM0();
+        PF_WAIT_VM(0);
         __builtin_amdgcn_s_barrier();
-        issue(kt + 3, nA, nB);
-        compute(cA, cB);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + 2, cA, cB);
+        __builtin_amdgcn_sched_barrier(0);
+        read(nA, nB, 0, fa);
+        mma(fb);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
     };
     issue(0, sA0, sB0);
     issue(1, sA1, sB1);
-    issue(2, sA2, sB2);
-    for (int k0 = 0; k0 < nk; k0 += PF_NST) {
-        step(k0, sA0, sB0, sA3, sB3);
+    PF_WAIT_VM(16);
+    __builtin_amdgcn_s_barrier();
+    read(sA0, sB0, 0, fa);
+    const int nk_main = nk & ~1;
+    for (int k0 = 0; k0 < nk_main; k0 += 2) {
+        step(k0, sA0, sB0, sA1, sB1);
         step(k0 + 1, sA1, sB1, sA0, sB0);
-        step(k0 + 2, sA2, sB2, sA1, sB1);
-        step(k0 + 3, sA3, sB3, sA2, sB2);
     }
+    if (nk & 1) step(nk_main, sA0, sB0, sA1, sB1);
     PF_WAIT_VM(0);
+    PF_WAIT_LGKM0();
 
     // acc[wb][tb][i]: weight row 8*(i/4) + 4*(lane/32) + i%4 of block wb,
     // token lane % 32 of block tb.
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int grow = row0 + wm * 64 + tb * 32 + (lane & 31);
+    for (int tb = 0; tb < 4; ++tb) {
+        const int grow = row0 + wm * 128 + tb * 32 + (lane & 31);
         if (grow >= row_end) continue;
         bf16* orow = out + (size_t)grow * N;
 #pragma unroll
@@ -440,7 +487,7 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
     const long tiles = (long)max_mt * n_nt;
     const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
     const int kid = GATED ? MOE_KERNEL_FFN_GATE_UP : MOE_KERNEL_FFN_DOWN;
-    if (K % (PF_BK * PF_NST) == 0) {
+    if (K % PF_BK == 0) {
         MOE_TIMED_LAUNCH(kid, s,
                          ffn_prefill_kernel<GATED><<<grid, PF_THREADS, 0, s>>>(
                              n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out));
