@@ -3,8 +3,8 @@
 // (ybb.press/quantum-computing/18594) §2.3 notes that decode is bound by
 // loading expert weights, which is what this kernel is shaped for.
 //
-// Each workgroup owns a strip of 16 weight rows of one expert (for gate/up the
-// same 16 rows of W1 and of W3) and its four waves split the reduction
+// Each workgroup owns a strip of 16 R weight rows of one expert (for gate/up
+// the same rows of W1 and of W3) and its four waves split the reduction
 // dimension.  A wave streams its rows in chunks of 128 * CPI k values.  In a
 // chunk, load instruction s reads bytes [64 s, 64 s + 64) of the chunk of every
 // row: the four lanes of a row read 64 contiguous bytes, and the 4 * CPI
@@ -36,16 +36,16 @@ __device__ __forceinline__ u32x4 load16_masked(const bf16* row, int k, int K) {
     return k < K ? v : z;
 }
 
-template <bool GATED, int CPI, int NCB, bool ALIGNED>
+template <bool GATED, int CPI, int NCB, bool ALIGNED, int R>
 __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
     int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ offsets,
     const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
     constexpr int NG = GATED ? 2 : 1;
     constexpr int NS = 4 * CPI;          // 32-wide slices per chunk
     constexpr int KCH = DC_KCH * CPI;  // k per chunk
-    __shared__ float red[DC_WAVES - 1][NCB][NG][4][kWave];
+    __shared__ float red[DC_WAVES - 1][R][NCB][NG][4][kWave];
     const int e = blockIdx.y;
-    const int n0 = blockIdx.x * DC_ROWS;
+    const int n0 = blockIdx.x * DC_ROWS * R;
     const int r0 = offsets[e];
     const int m = min(offsets[e + 1], n_rows) - r0;
     if (r0 < 0 || m <= 0) return;
@@ -58,19 +58,26 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
     const int per = (nch + DC_WAVES - 1) / DC_WAVES;
     const int c_beg = min(nch, wave * per);
     const int c_end = min(nch, c_beg + per);
-    const int wrow = min(n0 + rl, N - 1);
-    const bf16* wa = Wa + ((size_t)e * N + wrow) * K;
-    const bf16* wb = GATED ? Wb + ((size_t)e * N + wrow) * K : nullptr;
+    const bf16* wa[R];
+    const bf16* wb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int wrow = min(n0 + DC_ROWS * r + rl, N - 1);
+        wa[r] = Wa + ((size_t)e * N + wrow) * K;
+        wb[r] = GATED ? Wb + ((size_t)e * N + wrow) * K : nullptr;
+    }
     const int kl = g * 8;  // this lane's k offset inside each 32-wide slice
 
     for (int p0 = 0; p0 < m; p0 += 16 * NCB) {
         const int mp = min(m - p0, 16 * NCB);
         const int ncb = (mp + 15) / 16;
-        f32x4 acc[NCB][NG];
+        f32x4 acc[R][NCB][NG];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) acc[cb][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) acc[r][cb][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
         const bf16* arow[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -80,19 +87,21 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
         // after the token loads of chunk c, so waiting for the tokens of chunk c
         // (and the weights of chunk c, issued one step earlier) leaves chunk
         // c + 1 in flight while chunk c is multiplied.
-        u32x4 wc[NG][NS], wn[NG][NS];
-        auto load_w = [&](int c, u32x4 (&wd)[NG][NS]) {
+        u32x4 wc[R][NG][NS], wn[R][NG][NS];
+        auto load_w = [&](int c, u32x4 (&wd)[R][NG][NS]) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int k = c * KCH + s * 32 + kl;
-                if (ALIGNED) {  // K is a multiple of the chunk: every load is in range
-                    wd[0][s] = load16(wa + k);
-                    if (GATED) wd[NG - 1][s] = load16(wb + k);
-                } else {
-                    wd[0][s] = load16_masked(wa, k, K);
-                    if (GATED) wd[NG - 1][s] = load16_masked(wb, k, K);
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const int k = c * KCH + s * 32 + kl;
+                    if (ALIGNED) {  // K is a multiple of the chunk: every load is in range
+                        wd[r][0][s] = load16(wa[r] + k);
+                        if (GATED) wd[r][NG - 1][s] = load16(wb[r] + k);
+                    } else {
+                        wd[r][0][s] = load16_masked(wa[r], k, K);
+                        if (GATED) wd[r][NG - 1][s] = load16_masked(wb[r], k, K);
+                    }
                 }
-            }
         };
         if (c_beg < c_end) load_w(c_beg, wc);
         for (int c = c_beg; c < c_end; ++c) {
@@ -114,52 +123,63 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
 #pragma unroll
                     for (int s = 0; s < NS; ++s) {
                         const bf16x8 xb = as_bf16x8(xv[cb][s]);
-                        acc[cb][0] = mfma16(as_bf16x8(wc[0][s]), xb, acc[cb][0]);
-                        if (GATED) acc[cb][NG - 1] = mfma16(as_bf16x8(wc[NG - 1][s]), xb, acc[cb][NG - 1]);
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            acc[r][cb][0] = mfma16(as_bf16x8(wc[r][0][s]), xb, acc[r][cb][0]);
+                            if (GATED)
+                                acc[r][cb][NG - 1] = mfma16(as_bf16x8(wc[r][NG - 1][s]), xb, acc[r][cb][NG - 1]);
+                        }
                     }
                 }
             }
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-                for (int s = 0; s < NS; ++s) wc[gi][s] = wn[gi][s];
-        }
-        if (wave > 0) {
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
+            for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) red[wave - 1][cb][gi][i][lane] = acc[cb][gi][i];
+                    for (int s = 0; s < NS; ++s) wc[r][gi][s] = wn[r][gi][s];
+        }
+        if (wave > 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) red[wave - 1][r][cb][gi][i][lane] = acc[r][cb][gi][i];
         }
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                if (cb >= ncb) break;
-                // lane holds output (weight row 4g + i, token column rl) of this block
-                const int tcol = cb * 16 + rl;
-                float v[4];
+            for (int r = 0; r < R; ++r) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float s0 = acc[cb][0][i];
-                    float s1 = GATED ? acc[cb][NG - 1][i] : 0.0f;
+                for (int cb = 0; cb < NCB; ++cb) {
+                    if (cb >= ncb) break;
+                    // lane holds output (weight row 4g + i of block r, token column rl)
+                    const int tcol = cb * 16 + rl;
+                    float v[4];
 #pragma unroll
-                    for (int w = 0; w < DC_WAVES - 1; ++w) {
-                        s0 += red[w][cb][0][i][lane];
-                        if (GATED) s1 += red[w][cb][NG - 1][i][lane];
+                    for (int i = 0; i < 4; ++i) {
+                        float s0 = acc[r][cb][0][i];
+                        float s1 = GATED ? acc[r][cb][NG - 1][i] : 0.0f;
+#pragma unroll
+                        for (int w = 0; w < DC_WAVES - 1; ++w) {
+                            s0 += red[w][r][cb][0][i][lane];
+                            if (GATED) s1 += red[w][r][cb][NG - 1][i][lane];
+                        }
+                        v[i] = GATED ? silu(s0) * s1 : s0;
                     }
-                    v[i] = GATED ? silu(s0) * s1 : s0;
-                }
-                if (tcol < mp) {
-                    const int col = n0 + g * 4;
-                    bf16* o = out + (size_t)(r0 + p0 + tcol) * N + col;
-                    if (col + 3 < N) {
-                        bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-                        *reinterpret_cast<bf16x4*>(o) = pk;
-                    } else {
-                        for (int i = 0; i < 4; ++i)
-                            if (col + i < N) o[i] = (bf16)v[i];
+                    if (tcol < mp) {
+                        const int col = n0 + DC_ROWS * r + g * 4;
+                        bf16* o = out + (size_t)(r0 + p0 + tcol) * N + col;
+                        if (col + 3 < N) {
+                            bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+                            *reinterpret_cast<bf16x4*>(o) = pk;
+                        } else {
+                            for (int i = 0; i < 4; ++i)
+                                if (col + i < N) o[i] = (bf16)v[i];
+                        }
                     }
                 }
             }
@@ -174,14 +194,16 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* x
                                   const void* w2, void* act, void* h, hipStream_t s) {
     dim3 g1((F + DC_ROWS - 1) / DC_ROWS, E);
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_GATE_UP, s,
-                     ffn_decode_kernel<true, 1, 1, ALIGNED><<<g1, DC_WAVES * kWave, 0, s>>>(
+                     ffn_decode_kernel<true, 1, 1, ALIGNED, 1><<<g1, DC_WAVES * kWave, 0, s>>>(
                          n_rows, F, d, (const bf16*)x_perm, offsets, (const bf16*)w1, (const bf16*)w3,
                          (bf16*)act));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    dim3 g2((d + DC_ROWS - 1) / DC_ROWS, E);
+    // Two 16-row blocks per workgroup for the down projection: each token
+    // fragment (an L2 read of the long activation rows) feeds two MFMAs.
+    dim3 g2((d + 2 * DC_ROWS - 1) / (2 * DC_ROWS), E);
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
-                     ffn_decode_kernel<false, 1, 1, ALIGNED><<<g2, DC_WAVES * kWave, 0, s>>>(
+                     ffn_decode_kernel<false, 1, 1, ALIGNED, 2><<<g2, DC_WAVES * kWave, 0, s>>>(
                          n_rows, d, F, (const bf16*)act, offsets, (const bf16*)w2, nullptr, (bf16*)h));
     return hipGetLastError();
 }

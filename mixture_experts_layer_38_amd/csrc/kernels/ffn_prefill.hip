@@ -35,13 +35,12 @@
 
 namespace moe {
 
-constexpr int PF_BM = 256;          // token rows per tile
 constexpr int PF_BN = 256;          // weight rows per tile
 constexpr int PF_BK = 64;           // k per pipeline stage (128-byte tile rows)
 constexpr int PF_THREADS = 256;
+constexpr int PF_BM_MAX = 256;      // token rows per tile: 256, or 128 for small groups
 constexpr int PF_GM = 8;            // row tiles per group in the tile order
 constexpr int PF_XCD = 8;
-constexpr int PF_STAGE = PF_BM * PF_BK;  // bf16 elements of one operand stage (PF_BM == PF_BN)
 
 // Swizzle of the eight 16-byte chunks of a 128-byte tile row: row r keeps
 // chunk c in slot c ^ pf_swz(r), so fragment reads of consecutive rows (one
@@ -53,11 +52,11 @@ __device__ __forceinline__ int pf_swz(int r) { return (r ^ (r >> 3)) & 7; }
 // s_waitcnt immediate: lgkmcnt == 0, no wait on the other counters.
 #define PF_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
 
-int prefill_max_mtiles(int n_rows, int E) { return n_rows / PF_BM + E + 1; }
+int prefill_max_mtiles(int n_rows, int E) { return n_rows / 128 + E + 1; }
 
-// One block; thread e cuts expert e's rows into PF_BM-row tiles: *mt_count
+// One block; thread e cuts expert e's rows into bm-row tiles: *mt_count
 // row tiles, tile j of expert mt_expert[j] starting at grouped row mt_row0[j].
-__global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt,
+__global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int bm,
                                                        const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ mt_count,
                                                        int32_t* __restrict__ mt_expert,
@@ -67,7 +66,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt,
     const int lane = e & (kWave - 1);
     const int wv = e / kWave;
     const int rows = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-    const int nt = (rows + PF_BM - 1) / PF_BM;
+    const int nt = (rows + bm - 1) / bm;
     int incl = nt;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -82,23 +81,31 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt,
     if (e < E) {
         for (int j = 0; j < nt && start + j < max_mt; ++j) {
             mt_expert[start + j] = e;
-            mt_row0[start + j] = offsets[e] + j * PF_BM;
+            mt_row0[start + j] = offsets[e] + j * bm;
         }
     }
     if (e == E - 1) *mt_count = min(start + nt, max_mt);
 }
 
 // N: weight rows of one expert (gate/up: F, down: d); K: reduction length,
-// a multiple of PF_BK; n_nt: weight tiles per row tile.
-template <bool GATED>
+// a multiple of PF_BK; n_nt: weight tiles per row tile.  BM: token rows per
+// tile (256, or 128 for small expert groups); NSLOT: LDS stages in the ring.
+template <bool GATED, int BM, int NSLOT>
 __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ffn_prefill_kernel(
     int n_rows, int N, int K, int n_nt, const bf16* __restrict__ A,
     const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
     const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ offsets,
     const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
-    __shared__ __align__(1024) bf16 sA0[PF_STAGE], sA1[PF_STAGE];
-    __shared__ __align__(1024) bf16 sB0[PF_STAGE], sB1[PF_STAGE];
+    constexpr int SA = BM * PF_BK;      // bf16 elements of one A stage
+    constexpr int SB = PF_BN * PF_BK;   // bf16 elements of one B stage
+    constexpr int NTB = BM / 64;        // 32-row token blocks per wave
+    constexpr int NJA = BM / 32;        // A load instructions per wave per stage
+    constexpr int NJB = PF_BN / 32;     // B load instructions per wave per stage
+    constexpr int NLD = NJA + NJB;      // loads per wave per stage
+    static_assert(NSLOT >= 2 && NSLOT <= 3, "two or three slots");
+    __shared__ __align__(1024) bf16 sA0[SA], sA1[SA], sA2[NSLOT > 2 ? SA : 1];
+    __shared__ __align__(1024) bf16 sB0[SB], sB1[SB], sB2[NSLOT > 2 ? SB : 1];
     const int n_mt = *mt_count;
     const int tiles = n_mt * n_nt;
     const int per_xcd = (tiles + PF_XCD - 1) / PF_XCD;
@@ -119,20 +126,24 @@ void ffn_prefill_kernel(
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int lane = lane_id();
 
-    // Loads: a stage is 32 A and 32 B wave instructions of 8 rows x 128 bytes;
-    // wave w issues A rows [8 (w + 4 j), +8) for j = 0..7, and the same B
-    // rows.  Lane p fills slot p % 8 of tile row p / 8 of its instruction,
-    // fetching the chunk that the swizzle puts there.
+    // Loads: a stage is BM/8 A and 32 B wave instructions of 8 rows x 128
+    // bytes; wave w issues rows [8 (w + 4 j), +8) of each.  Lane p fills slot
+    // p % 8 of tile row p / 8 of its instruction, fetching the chunk that the
+    // swizzle puts there.
     const int lr = lane >> 3;
     const int ls = lane & 7;
-    const bf16* a_src[8];
-    const bf16* b_src[8];
+    const bf16* a_src[NJA];
+    const bf16* b_src[NJB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int tr = 8 * (wave + 4 * j) + lr;  // tile row, A and B alike
-        const int c = ls ^ pf_swz(tr);
+    for (int j = 0; j < NJA; ++j) {
+        const int tr = 8 * (wave + 4 * j) + lr;
         const int r = min(row0 + tr, n_rows - 1);
-        a_src[j] = A + (size_t)r * K + c * 8;
+        a_src[j] = A + (size_t)r * K + (ls ^ pf_swz(tr)) * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < NJB; ++j) {
+        const int tr = 8 * (wave + 4 * j) + lr;
+        const int c = ls ^ pf_swz(tr);
         if (GATED) {
             // tile rows [128 w, 128 w + 128) = W1, W3, W1, W3 blocks of 32 rows
             // for features nt*128 + 64 w + [0, 64)
@@ -150,36 +161,37 @@ void ffn_prefill_kernel(
     auto issue = [&](int kt, bf16* dA, bf16* dB) {
         const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int off = 8 * (wave + 4 * j) * PF_BK;
+        for (int j = 0; j < NJA; ++j)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[j] + ko),
-                                             (__attribute__((address_space(3))) void*)(dA + off), 16, 0, 0);
+                                             (__attribute__((address_space(3))) void*)(dA + 8 * (wave + 4 * j) * PF_BK),
+                                             16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NJB; ++j)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b_src[j] + ko),
-                                             (__attribute__((address_space(3))) void*)(dB + off), 16, 0, 0);
-        }
+                                             (__attribute__((address_space(3))) void*)(dB + 8 * (wave + 4 * j) * PF_BK),
+                                             16, 0, 0);
     };
 
-    const int wm = wave & 1;   // token block of 128
-    const int wn = wave >> 1;  // weight block of 128
-    f32x16 acc[4][4];
+    const int wm = wave & 1;   // token half of the tile (BM / 2 rows)
+    const int wn = wave >> 1;  // weight half of the tile (128 rows)
+    f32x16 acc[4][NTB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NTB; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
     // Fragment rows: weight rows wn*128 + 32 wb + lane%32, token rows
-    // wm*128 + 32 tb + lane%32; their swizzles are fixed for the whole tile.
+    // wm*BM/2 + 32 tb + lane%32; their swizzles are fixed for the whole tile.
     const int fhalf = lane >> 5;
-    int wsw[4], tsw[4];
+    int wsw[4], tsw[NTB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        wsw[i] = pf_swz(wn * 128 + i * 32 + (lane & 31));
-        tsw[i] = pf_swz(wm * 128 + i * 32 + (lane & 31));
-    }
+    for (int i = 0; i < 4; ++i) wsw[i] = pf_swz(wn * 128 + i * 32 + (lane & 31));
+#pragma unroll
+    for (int i = 0; i < NTB; ++i) tsw[i] = pf_swz(wm * (BM / 2) + i * 32 + (lane & 31));
     struct Frags {
-        bf16x8 w[4], t[4];
+        bf16x8 w[4], t[NTB];
     };
     // 16-wide k quarter q of a stage: chunk 2q + (lane / 32).
     auto read = [&](const bf16* cA, const bf16* cB, int q, Frags& f) {
@@ -189,36 +201,38 @@ void ffn_prefill_kernel(
             f.w[wb] = *reinterpret_cast<const bf16x8*>(
                 &cB[(wn * 128 + wb * 32 + (lane & 31)) * PF_BK + (c ^ wsw[wb]) * 8]);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < NTB; ++tb)
             f.t[tb] = *reinterpret_cast<const bf16x8*>(
-                &cA[(wm * 128 + tb * 32 + (lane & 31)) * PF_BK + (c ^ tsw[tb]) * 8]);
+                &cA[(wm * (BM / 2) + tb * 32 + (lane & 31)) * PF_BK + (c ^ tsw[tb]) * 8]);
     };
     auto mma = [&](const Frags& f) {
 #pragma unroll
         for (int wb = 0; wb < 4; ++wb)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[wb][tb] = mfma32(f.w[wb], f.t[tb], acc[wb][tb]);
+            for (int tb = 0; tb < NTB; ++tb) acc[wb][tb] = mfma32(f.w[wb], f.t[tb], acc[wb][tb]);
     };
-    // Interleave: one MFMA, then one LDS fragment read, eight times, then the
-    // remaining eight MFMAs (the reads issue in the shadow of the MFMAs).
+    // Interleave: one MFMA, then one LDS fragment read, for every read of the
+    // next quarter, then the remaining MFMAs (the reads issue in the shadow of
+    // the MFMAs).
     auto interleave = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4 + NTB; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NTB - (4 + NTB), 0);
     };
-    // Stage kt lives in slot kt % 2 and is multiplied in four 16-wide
+    // Stage kt lives in slot kt % NSLOT and is multiplied in four 16-wide
     // quarters; the LDS reads of each quarter overlap the MFMAs of the quarter
     // before.  After the third quarter's MFMAs: wait until this wave's reads
-    // of slot kt % 2 are done and its loads of stage kt + 1 have landed; a
-    // barrier then makes stage kt + 1 visible to every wave and tells every
-    // wave that slot kt % 2 is free, and the loads of stage kt + 2 go there;
-    // the first quarter of stage kt + 1 is read during the last quarter's
-    // MFMAs.  Every step issues the same loads and reads (clamped to the last
-    // stage at the end, into a slot no later step reads), so the counts of
-    // loads in flight are the same on every path.
+    // of slot kt % NSLOT are done and its loads of stage kt + 1 have landed
+    // (the loads of later stages may still be in flight); a barrier then makes
+    // stage kt + 1 visible to every wave and tells every wave that slot
+    // kt % NSLOT is free, and the loads of stage kt + NSLOT go there; the first
+    // quarter of stage kt + 1 is read during the last quarter's MFMAs.  Every
+    // step issues the same loads and reads (clamped to the last stage at the
+    // end, into slots no later step reads), so the counts of loads in flight
+    // are the same on every path.
     Frags fa, fb;
     auto step = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB) {
         read(cA, cB, 1, fb);
@@ -234,10 +248,10 @@ void ffn_prefill_kernel(
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         PF_WAIT_LGKM0();
-        PF_WAIT_VM(0);
+        PF_WAIT_VM(NLD * (NSLOT - 2));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(kt + 2, cA, cB);
+        issue(kt + NSLOT, cA, cB);
         __builtin_amdgcn_sched_barrier(0);
         read(nA, nB, 0, fa);
         mma(fb);
@@ -246,23 +260,35 @@ void ffn_prefill_kernel(
     };
     issue(0, sA0, sB0);
     issue(1, sA1, sB1);
-    PF_WAIT_VM(16);
+    if (NSLOT > 2) issue(2, sA2, sB2);
+    PF_WAIT_VM(NLD * (NSLOT - 1));
     __builtin_amdgcn_s_barrier();
     read(sA0, sB0, 0, fa);
-    const int nk_main = nk & ~1;
-    for (int k0 = 0; k0 < nk_main; k0 += 2) {
-        step(k0, sA0, sB0, sA1, sB1);
-        step(k0 + 1, sA1, sB1, sA0, sB0);
+    const int nk_main = nk - nk % NSLOT;
+    if (NSLOT == 2) {
+        for (int k0 = 0; k0 < nk_main; k0 += 2) {
+            step(k0, sA0, sB0, sA1, sB1);
+            step(k0 + 1, sA1, sB1, sA0, sB0);
+        }
+        if (nk - nk_main > 0) step(nk_main, sA0, sB0, sA1, sB1);
+    } else {
+        for (int k0 = 0; k0 < nk_main; k0 += 3) {
+            step(k0, sA0, sB0, sA1, sB1);
+            step(k0 + 1, sA1, sB1, sA2, sB2);
+            step(k0 + 2, sA2, sB2, sA0, sB0);
+        }
+        // The last nk % 3 stages start again at slot 0.
+        if (nk - nk_main > 0) step(nk_main, sA0, sB0, sA1, sB1);
+        if (nk - nk_main > 1) step(nk_main + 1, sA1, sB1, sA2, sB2);
     }
-    if (nk & 1) step(nk_main, sA0, sB0, sA1, sB1);
     PF_WAIT_VM(0);
     PF_WAIT_LGKM0();
 
     // acc[wb][tb][i]: weight row 8*(i/4) + 4*(lane/32) + i%4 of block wb,
     // token lane % 32 of block tb.
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int grow = row0 + wm * 128 + tb * 32 + (lane & 31);
+    for (int tb = 0; tb < NTB; ++tb) {
+        const int grow = row0 + wm * (BM / 2) + tb * 32 + (lane & 31);
         if (grow >= row_end) continue;
         bf16* orow = out + (size_t)grow * N;
 #pragma unroll
@@ -479,7 +505,7 @@ size_t prefill_ws_bytes(int n_rows, int E) {
 }
 
 template <bool GATED>
-static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int max_mt,
+static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int max_mt, int bm,
                                       const bf16* A, const int32_t* mt_count,
                                       const int32_t* mt_expert, const int32_t* mt_row0,
                                       const int32_t* offsets, const bf16* Wa, const bf16* Wb,
@@ -488,9 +514,14 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
     const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
     const int kid = GATED ? MOE_KERNEL_FFN_GATE_UP : MOE_KERNEL_FFN_DOWN;
     if (K % PF_BK == 0) {
-        MOE_TIMED_LAUNCH(kid, s,
-                         ffn_prefill_kernel<GATED><<<grid, PF_THREADS, 0, s>>>(
-                             n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out));
+        if (bm == 256)
+            MOE_TIMED_LAUNCH(kid, s,
+                             (ffn_prefill_kernel<GATED, 256, 2><<<grid, PF_THREADS, 0, s>>>(
+                                 n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
+        else
+            MOE_TIMED_LAUNCH(kid, s,
+                             (ffn_prefill_kernel<GATED, 128, 3><<<grid, PF_THREADS, 0, s>>>(
+                                 n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
         return hipGetLastError();
     }
     static bool attr_set = false;
@@ -507,22 +538,31 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
     return hipGetLastError();
 }
 
+// Row-tile height: 256 when the expert groups are large on average, else 128
+// (less wasted MFMA work on partly filled tiles).  The generic variant always
+// uses 256-row tiles.
+static int prefill_bm(int n_rows, int E, int d, int F) {
+    if (d % PF_BK != 0 || F % PF_BK != 0) return 256;
+    return n_rows >= 512 * E ? 256 : 128;
+}
+
 hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* x_perm,
                               const int32_t* offsets, const void* w1, const void* w3,
                               const void* w2, void* act, void* h, void* ws, hipStream_t s) {
     const int max_mt = prefill_max_mtiles(n_rows, E);
+    const int bm = prefill_bm(n_rows, E, d, F);
     int32_t* mt_count = reinterpret_cast<int32_t*>(ws);
     int32_t* mt_expert = mt_count + 1;
     int32_t* mt_row0 = mt_expert + max_mt;
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_PLAN, s,
-                     ffn_plan_kernel<<<1, 1024, 0, s>>>(E, max_mt, offsets, mt_count, mt_expert, mt_row0));
+                     ffn_plan_kernel<<<1, 1024, 0, s>>>(E, max_mt, bm, offsets, mt_count, mt_expert, mt_row0));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, (const bf16*)x_perm,
+    err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, (const bf16*)x_perm,
                                     mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
                                     (const bf16*)w3, (bf16*)act, s);
     if (err != hipSuccess) return err;
-    return launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt,
+    return launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
                                       (const bf16*)act, mt_count, mt_expert, mt_row0, offsets,
                                       (const bf16*)w2, nullptr, (bf16*)h, s);
 }
