@@ -176,7 +176,10 @@ moe_status moe_combine(const moe_problem* p, const void* h, const int32_t* assig
                        const float* topk_w, void* y, void* stream);
 
 /* Whole layer: route -> dispatch -> expert FFN -> combine on one stream, with
- * every intermediate in `ws` (moe_workspace_size bytes).
+ * every intermediate in `ws` (moe_workspace_size bytes).  The grouped token
+ * rows are not materialised here: the expert FFN reads each group's token
+ * rows from x through the dispatch's row map ([SERVE] §10.4, a fused MoE
+ * kernel avoids the separate permute pass).
  *   x [T,d], w_router [d,E], w1/w3 [E,F,d], w2 [E,d,F] in dtype;
  *   logit_bias [E] fp32 or NULL; y [T,d] dtype out;
  *   dbg: NULL, or device pointers that receive intermediate results. */

@@ -35,6 +35,14 @@ __device__ __forceinline__ u32x4 load16_or_zero(const void* p, bool valid) {
     return valid ? load16(p) : z;
 }
 
+// Row of the first GEMM operand for grouped row r: r itself, or the token
+// of assignment rowmap[r] (K slots per token; -1 reads token 0).
+__device__ __forceinline__ int src_row(const int32_t* rowmap, int topk, int r) {
+    if (!rowmap) return r;
+    const int a = rowmap[r];
+    return a < 0 ? 0 : a / topk;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // Wave-wide reductions (64 lanes).

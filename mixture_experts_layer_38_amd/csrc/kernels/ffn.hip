@@ -9,11 +9,11 @@
 
 namespace moe {
 
-hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* x_perm, const int32_t* offsets,
-                             const void* w1, const void* w3, const void* w2, void* act, void* h,
-                             hipStream_t s);
-hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* x_perm,
-                              const int32_t* offsets, const void* w1, const void* w3,
+hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* A, const int32_t* rowmap,
+                             int topk, const int32_t* offsets, const void* w1, const void* w3,
+                             const void* w2, void* act, void* h, hipStream_t s);
+hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, const int32_t* rowmap,
+                              int topk, const int32_t* offsets, const void* w1, const void* w3,
                               const void* w2, void* act, void* h, void* ws, hipStream_t s);
 size_t prefill_ws_bytes(int n_rows, int E);
 
@@ -32,6 +32,7 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int 
 
 __global__ __launch_bounds__(256) void ffn_f32_gate_up_kernel(int n_rows, int E, int F, int d,
                                                              const float* __restrict__ A,
+                                                             const int32_t* __restrict__ rowmap, int topk,
                                                              const int32_t* __restrict__ offsets,
                                                              const float* __restrict__ w1,
                                                              const float* __restrict__ w3,
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void ffn_f32_gate_up_kernel(int n_rows, int E,
     const int row = (int)(i / F);
     const int f = (int)(i - (size_t)row * F);
     const int e = expert_of_row(offsets, E, row);
-    const float* a = A + (size_t)row * d;
+    const float* a = A + (size_t)src_row(rowmap, topk, row) * d;
     const float* r1 = w1 + ((size_t)e * F + f) * d;
     const float* r3 = w3 + ((size_t)e * F + f) * d;
     float g1 = 0.0f, g3 = 0.0f;
@@ -78,15 +79,15 @@ size_t ffn_ws_bytes(int T, int K, int E, int /*d*/, int /*F*/, int dtype) {
     return prefill_ws_bytes(T * K, E);
 }
 
-hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* x_perm,
-                      const int32_t* offsets, const void* w1, const void* w3, const void* w2,
-                      void* act, void* h, void* ws, hipStream_t s) {
+hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* A,
+                      const int32_t* rowmap, const int32_t* offsets, const void* w1,
+                      const void* w3, const void* w2, void* act, void* h, void* ws, hipStream_t s) {
     const int n = T * K;
     if (dtype == MOE_DTYPE_F32) {
         const size_t n1 = (size_t)n * F, n2 = (size_t)n * d;
         MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_GATE_UP, s,
                          ffn_f32_gate_up_kernel<<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
-                             n, E, F, d, (const float*)x_perm, offsets, (const float*)w1,
+                             n, E, F, d, (const float*)A, rowmap, K, offsets, (const float*)w1,
                              (const float*)w3, (float*)act));
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -96,8 +97,8 @@ hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* 
         return hipGetLastError();
     }
     if (use_decode(T, dtype))
-        return launch_ffn_decode(n, E, d, F, x_perm, offsets, w1, w3, w2, act, h, s);
-    return launch_ffn_prefill(n, E, d, F, x_perm, offsets, w1, w3, w2, act, h, ws, s);
+        return launch_ffn_decode(n, E, d, F, A, rowmap, K, offsets, w1, w3, w2, act, h, s);
+    return launch_ffn_prefill(n, E, d, F, A, rowmap, K, offsets, w1, w3, w2, act, h, ws, s);
 }
 
 }  // namespace moe

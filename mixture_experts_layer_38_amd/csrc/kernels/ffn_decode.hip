@@ -38,8 +38,9 @@ __device__ __forceinline__ u32x4 load16_masked(const bf16* row, int k, int K) {
 
 template <bool GATED, int CPI, int NCB, bool ALIGNED, int R>
 __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
-    int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ offsets,
-    const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
+    int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
+    const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
+    bf16* __restrict__ out) {
     constexpr int NG = GATED ? 2 : 1;
     constexpr int NS = 4 * CPI;          // 32-wide slices per chunk
     constexpr int KCH = DC_KCH * CPI;  // k per chunk
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
         const bf16* arow[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-            arow[cb] = A + (size_t)(r0 + p0 + min(cb * 16 + rl, mp - 1)) * K;
+            arow[cb] = A + (size_t)src_row(rowmap, topk, r0 + p0 + min(cb * 16 + rl, mp - 1)) * K;
 
         // Double buffer in registers: the weight loads of chunk c + 1 are issued
         // after the token loads of chunk c, so waiting for the tokens of chunk c
@@ -189,13 +190,14 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
 }
 
 template <bool ALIGNED>
-static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* x_perm,
-                                  const int32_t* offsets, const void* w1, const void* w3,
-                                  const void* w2, void* act, void* h, hipStream_t s) {
+static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A,
+                                  const int32_t* rowmap, int topk, const int32_t* offsets,
+                                  const void* w1, const void* w3, const void* w2, void* act,
+                                  void* h, hipStream_t s) {
     dim3 g1((F + DC_ROWS - 1) / DC_ROWS, E);
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_GATE_UP, s,
                      ffn_decode_kernel<true, 1, 1, ALIGNED, 1><<<g1, DC_WAVES * kWave, 0, s>>>(
-                         n_rows, F, d, (const bf16*)x_perm, offsets, (const bf16*)w1, (const bf16*)w3,
+                         n_rows, F, d, (const bf16*)A, rowmap, topk, offsets, (const bf16*)w1, (const bf16*)w3,
                          (bf16*)act));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -204,16 +206,16 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* x
     dim3 g2((d + 2 * DC_ROWS - 1) / (2 * DC_ROWS), E);
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
                      ffn_decode_kernel<false, 1, 1, ALIGNED, 2><<<g2, DC_WAVES * kWave, 0, s>>>(
-                         n_rows, d, F, (const bf16*)act, offsets, (const bf16*)w2, nullptr, (bf16*)h));
+                         n_rows, d, F, (const bf16*)act, nullptr, 1, offsets, (const bf16*)w2, nullptr, (bf16*)h));
     return hipGetLastError();
 }
 
-hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* x_perm, const int32_t* offsets,
-                             const void* w1, const void* w3, const void* w2, void* act, void* h,
-                             hipStream_t s) {
+hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* A, const int32_t* rowmap,
+                             int topk, const int32_t* offsets, const void* w1, const void* w3,
+                             const void* w2, void* act, void* h, hipStream_t s) {
     if (d % DC_KCH == 0 && F % DC_KCH == 0)
-        return launch_decode_t<true>(n_rows, E, d, F, x_perm, offsets, w1, w3, w2, act, h, s);
-    return launch_decode_t<false>(n_rows, E, d, F, x_perm, offsets, w1, w3, w2, act, h, s);
+        return launch_decode_t<true>(n_rows, E, d, F, A, rowmap, topk, offsets, w1, w3, w2, act, h, s);
+    return launch_decode_t<false>(n_rows, E, d, F, A, rowmap, topk, offsets, w1, w3, w2, act, h, s);
 }
 
 }  // namespace moe

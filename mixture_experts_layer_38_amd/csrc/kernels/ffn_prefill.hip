@@ -94,7 +94,7 @@ template <bool GATED, int BM, int NSLOT>
 __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ffn_prefill_kernel(
     int n_rows, int N, int K, int n_nt, const bf16* __restrict__ A,
-    const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
+    const int32_t* __restrict__ rowmap, int topk, const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
     const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ offsets,
     const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
     constexpr int SA = BM * PF_BK;      // bf16 elements of one A stage
@@ -137,7 +137,7 @@ void ffn_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < NJA; ++j) {
         const int tr = 8 * (wave + 4 * j) + lr;
-        const int r = min(row0 + tr, n_rows - 1);
+        const int r = src_row(rowmap, topk, min(row0 + tr, n_rows - 1));
         a_src[j] = A + (size_t)r * K + (ls ^ pf_swz(tr)) * 8;
     }
 #pragma unroll
@@ -346,9 +346,10 @@ constexpr size_t PG_LDS_BYTES = 4 * PG_TILE_ELEMS * sizeof(bf16);
 template <bool GATED>
 __global__ __launch_bounds__(PG_THREADS) void ffn_prefill_generic_kernel(
     int n_rows, int N, int K, int n_nt, const bf16* __restrict__ A,
-    const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
-    const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ offsets,
-    const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
+    const int32_t* __restrict__ rowmap, int topk, const int32_t* __restrict__ mt_count,
+    const int32_t* __restrict__ mt_expert, const int32_t* __restrict__ mt_row0,
+    const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
+    bf16* __restrict__ out) {
     extern __shared__ __align__(16) bf16 smem[];
     const int n_mt = *mt_count;
     const int tiles = n_mt * n_nt;
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(PG_THREADS) void ffn_prefill_generic_kernel(
     const bf16* b_src[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int r = min(row0 + lr + 64 * j, n_rows - 1);
+        const int r = src_row(rowmap, topk, min(row0 + lr + 64 * j, n_rows - 1));
         a_src[j] = A + (size_t)r * K + lc;
         const int br = lr + 64 * j;  // weight row inside the tile
         if (GATED) {
@@ -506,7 +507,8 @@ size_t prefill_ws_bytes(int n_rows, int E) {
 
 template <bool GATED>
 static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int max_mt, int bm,
-                                      const bf16* A, const int32_t* mt_count,
+                                      const bf16* A, const int32_t* rowmap, int topk,
+                                      const int32_t* mt_count,
                                       const int32_t* mt_expert, const int32_t* mt_row0,
                                       const int32_t* offsets, const bf16* Wa, const bf16* Wb,
                                       bf16* out, hipStream_t s) {
@@ -517,11 +519,11 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
         if (bm == 256)
             MOE_TIMED_LAUNCH(kid, s,
                              (ffn_prefill_kernel<GATED, 256, 2><<<grid, PF_THREADS, 0, s>>>(
-                                 n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
+                                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
         else
             MOE_TIMED_LAUNCH(kid, s,
                              (ffn_prefill_kernel<GATED, 128, 3><<<grid, PF_THREADS, 0, s>>>(
-                                 n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
+                                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
         return hipGetLastError();
     }
     static bool attr_set = false;
@@ -534,7 +536,7 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
     }
     MOE_TIMED_LAUNCH(kid, s,
                      ffn_prefill_generic_kernel<GATED><<<grid, PG_THREADS, PG_LDS_BYTES, s>>>(
-                         n_rows, N, K, n_nt, A, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out));
+                         n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out));
     return hipGetLastError();
 }
 
@@ -546,8 +548,8 @@ static int prefill_bm(int n_rows, int E, int d, int F) {
     return n_rows >= 512 * E ? 256 : 128;
 }
 
-hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* x_perm,
-                              const int32_t* offsets, const void* w1, const void* w3,
+hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, const int32_t* rowmap,
+                              int topk, const int32_t* offsets, const void* w1, const void* w3,
                               const void* w2, void* act, void* h, void* ws, hipStream_t s) {
     const int max_mt = prefill_max_mtiles(n_rows, E);
     const int bm = prefill_bm(n_rows, E, d, F);
@@ -558,12 +560,12 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* x_per
                      ffn_plan_kernel<<<1, 1024, 0, s>>>(E, max_mt, bm, offsets, mt_count, mt_expert, mt_row0));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, (const bf16*)x_perm,
-                                    mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
+    err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, (const bf16*)A,
+                                    rowmap, topk, mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
                                     (const bf16*)w3, (bf16*)act, s);
     if (err != hipSuccess) return err;
     return launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
-                                      (const bf16*)act, mt_count, mt_expert, mt_row0, offsets,
+                                      (const bf16*)act, nullptr, 1, mt_count, mt_expert, mt_row0, offsets,
                                       (const bf16*)w2, nullptr, (bf16*)h, s);
 }
 

@@ -43,9 +43,13 @@ hipError_t launch_dispatch(int T, int K, int E, int d, int dtype, int capacity,
 
 // ---- grouped expert FFN ----------------------------------------------------
 size_t ffn_ws_bytes(int T, int K, int E, int d, int F, int dtype);
-hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* x_perm,
-                      const int32_t* offsets, const void* w1, const void* w3, const void* w2,
-                      void* act, void* h, void* ws, hipStream_t s);
+// A: the grouped rows [T*K, d] when rowmap is NULL; otherwise the token rows
+// x [T, d], and grouped row r reads token rowmap[r] / K (rowmap = row_assign
+// of the dispatch; -1 past the kept rows reads token 0, whose results are
+// never stored).
+hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* A,
+                      const int32_t* rowmap, const int32_t* offsets, const void* w1,
+                      const void* w3, const void* w2, void* act, void* h, void* ws, hipStream_t s);
 
 // ---- combine / aux / bias --------------------------------------------------
 hipError_t launch_combine(int T, int K, int d, int dtype, const void* h,

@@ -65,7 +65,7 @@ static size_t elem_bytes(const moe_problem* p) { return p->dtype == MOE_DTYPE_F3
 // ---- workspace layout of moe_forward ------------------------------------------------
 struct ForwardLayout {
     size_t logits, probs, prob_sum, ids, w, counts, kept, offsets, assign_row, row_assign;
-    size_t x_perm, act, h, route_ws, disp_ws, ffn_ws, total;
+    size_t act, h, route_ws, disp_ws, ffn_ws, total;
 };
 
 static ForwardLayout forward_layout(const moe_problem* p) {
@@ -88,7 +88,6 @@ static ForwardLayout forward_layout(const moe_problem* p) {
     L.offsets = take((E + 1) * 4);
     L.assign_row = take(n * 4);
     L.row_assign = take(n * 4);
-    L.x_perm = take(n * d * es);
     L.act = take(n * F * es);
     L.h = take(n * d * es);
     L.route_ws = take(router_ws_bytes(p->T, p->d_model, p->n_experts, p->dtype));
@@ -234,7 +233,8 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x_perm, const int32_
     if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGNMENT;
     return hip_status(launch_ffn(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype,
-                                 x_perm, offsets, w1, w3, w2, act, h, ws, (hipStream_t)stream));
+                                 x_perm, nullptr, offsets, w1, w3, w2, act, h, ws,
+                                 (hipStream_t)stream));
 }
 
 moe_status moe_combine(const moe_problem* p, const void* h, const int32_t* assign_row,
@@ -286,7 +286,6 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     int32_t* offsets = D.offsets ? D.offsets : (int32_t*)(base + L.offsets);
     int32_t* assign_row = D.assign_row ? D.assign_row : (int32_t*)(base + L.assign_row);
     int32_t* row_assign = D.row_assign ? D.row_assign : (int32_t*)(base + L.row_assign);
-    void* x_perm = base + L.x_perm;
     void* act = base + L.act;
     void* h = base + L.h;
     hipStream_t s = (hipStream_t)stream;
@@ -294,12 +293,14 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
                                    logit_bias, logits, D.probs, D.prob_sum, ids, w,
                                    base + L.route_ws, s);
     if (err != hipSuccess) return MOE_ERR_HIP;
-    err = launch_dispatch(p->T, p->top_k, p->n_experts, p->d_model, p->dtype, p->capacity, ids, x,
-                          counts, kept, offsets, assign_row, row_assign, x_perm,
+    // The grouped token rows are never materialised: the first GEMM reads
+    // token row_assign[r] / K for its grouped row r.
+    err = launch_dispatch(p->T, p->top_k, p->n_experts, p->d_model, p->dtype, p->capacity, ids,
+                          nullptr, counts, kept, offsets, assign_row, row_assign, nullptr,
                           base + L.disp_ws, s);
     if (err != hipSuccess) return MOE_ERR_HIP;
-    err = launch_ffn(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype, x_perm, offsets,
-                     w1, w3, w2, act, h, base + L.ffn_ws, s);
+    err = launch_ffn(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype, x, row_assign,
+                     offsets, w1, w3, w2, act, h, base + L.ffn_ws, s);
     if (err != hipSuccess) return MOE_ERR_HIP;
     err = launch_combine(p->T, p->top_k, p->d_model, p->dtype, h, assign_row, w, y, s);
     return hip_status(err);
