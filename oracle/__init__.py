@@ -52,6 +52,10 @@ class Oracle:
         lib.oracle_aux_loss.restype = ctypes.c_double
         lib.oracle_bias_update.argtypes = [i64, i64, i64, vp, f32, vp]
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_z_loss.argtypes = [i64, i64, vp]
+        lib.oracle_z_loss.restype = ctypes.c_double
+        lib.oracle_aux_topk.argtypes = [i64, i64, i64, vp, vp, vp]
+        lib.oracle_aux_topk.restype = ctypes.c_double
         for name in ("oracle_router_logits", "oracle_route", "oracle_dispatch",
                      "oracle_expert", "oracle_layer_output", "oracle_bias_update"):
             getattr(lib, name).restype = None
@@ -135,6 +139,18 @@ class Oracle:
         probs = np.ascontiguousarray(probs, np.float64)
         T, E = probs.shape
         return float(self.lib.oracle_aux_loss(T, E, K, _p(counts), _p(probs)))
+
+    def z_loss(self, logits: np.ndarray) -> float:
+        logits = np.ascontiguousarray(logits, np.float32)
+        T, E = logits.shape
+        return float(self.lib.oracle_z_loss(T, E, _p(logits)))
+
+    def aux_topk(self, counts: np.ndarray, ids: np.ndarray, probs: np.ndarray) -> float:
+        counts = np.ascontiguousarray(counts, np.int32)
+        ids = np.ascontiguousarray(ids, np.int32)
+        probs = np.ascontiguousarray(probs, np.float64)
+        T, E = probs.shape
+        return float(self.lib.oracle_aux_topk(T, E, ids.shape[1], _p(counts), _p(ids), _p(probs)))
 
     def bias_update(self, counts: np.ndarray, T: int, K: int, alpha: float,
                     bias: np.ndarray) -> np.ndarray:

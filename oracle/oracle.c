@@ -239,3 +239,37 @@ void oracle_bias_update(int64_t T, int64_t E, int64_t K, const int32_t* counts,
             bias[e] = bias[e] + alpha;
     }
 }
+
+/* [NOTES] §3.2: the z-loss squares each token's log-sum-exp of the router
+ * scores (it keeps the scores from growing); the scores are the router's own
+ * output, before the per-expert balancing bias of [ENG] §1.2. */
+double oracle_z_loss(int64_t T, int64_t E, const float* logits) {
+    double total = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        double m = logits[t * E];
+        for (int64_t e = 1; e < E; ++e)
+            if (logits[t * E + e] > m) m = logits[t * E + e];
+        double s = 0.0;
+        for (int64_t e = 0; e < E; ++e) s += exp((double)logits[t * E + e] - m);
+        double lse = m + log(s);
+        total += lse * lse;
+    }
+    return total / (double)T;
+}
+
+/* [NOTES] §3.2: the approximate aux loss keeps only the probabilities of the
+ * experts each token selected (the soft assignment to the other experts is
+ * not counted). */
+double oracle_aux_topk(int64_t T, int64_t E, int64_t K, const int32_t* counts,
+                       const int32_t* ids, const double* probs) {
+    double sum_fp = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+        const double frac = (double)counts[e] / ((double)T * (double)K);
+        double chosen = 0.0; /* probability mass of e over the tokens that chose e */
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t k = 0; k < K; ++k)
+                if (ids[t * K + k] == e) chosen += probs[t * E + e];
+        sum_fp += frac * (chosen / (double)T);
+    }
+    return sum_fp * (double)E;
+}

@@ -66,6 +66,17 @@ double oracle_aux_loss(int64_t T, int64_t E, int64_t K, const int32_t* counts,
 void oracle_bias_update(int64_t T, int64_t E, int64_t K, const int32_t* counts,
                         float alpha, float* bias);
 
+/* Router z-loss ([NOTES] §3.2): (1/T) sum_t (log sum_e exp(logits[t,e]))^2,
+ * over the router scores before any per-expert bias.  logits [T,E] fp32. */
+double oracle_z_loss(int64_t T, int64_t E, const float* logits);
+
+/* The cheaper auxiliary loss of [NOTES] §3.2 that counts only the
+ * probabilities of the K chosen experts: E * sum_e f_e * P'_e with
+ * f_e = counts[e] / (T*K) and P'_e = (1/T) sum_t sum_k [ids[t,k] == e] probs[t,e]
+ * (probs: the routing softmax over all E, bias included). */
+double oracle_aux_topk(int64_t T, int64_t E, int64_t K, const int32_t* counts,
+                       const int32_t* ids, const double* probs);
+
 /* Number of OpenMP threads the oracle runs with. */
 int oracle_num_threads(void);
 

@@ -415,4 +415,63 @@ def pin_bias_update_sign_rule(orc):
         assert abs(float(got.astype(np.float64).sum()) - float(alpha) * (n_under - n_over)) < 1e-9
 
 
+# --------------------------------------------------------------------------
+# router regularisers (notes §3.2)
+# --------------------------------------------------------------------------
+
+def pin_router_losses_hand(orc):
+    """Hand-worked top-K aux and z-loss cases (notes §3.2), values derived in the fixture."""
+    g = _golden("router_losses_hand.json")
+    c = g["aux_case"]
+    counts = np.array(c["counts"], np.int32)
+    probs = np.array(c["probs"])
+    got = orc.aux_topk(counts, np.array(c["ids"], np.int32), probs)
+    assert abs(got - c["expect_aux_topk"]) < 1e-15, got
+    assert abs(orc.aux_loss(counts, probs, 1) - c["expect_aux"]) < 1e-15
+    z = orc.z_loss(np.array(g["z_case"]["logits"], np.float32))
+    # the fixture's ln 3 is rounded to fp32 on the way in; bound the effect
+    assert abs(z - g["z_case"]["expect_z"]) < 1e-6, z
+
+
+def pin_z_loss_closed_forms(orc):
+    """Equal scores c over E experts: log-sum-exp = c + ln E, so z = mean_t (c_t + ln E)^2;
+    one expert: z = mean of the squared scores."""
+    r = _rng(21)
+    for E in (1, 2, 8, 64):
+        c = (r.standard_normal(13) * 3).astype(np.float32)
+        logits = np.repeat(c[:, None], E, axis=1)
+        want = np.mean((c.astype(np.float64) + math.log(E)) ** 2)
+        assert abs(orc.z_loss(logits) - want) < 1e-12 * max(1.0, want), E
+    l1 = r.standard_normal((9, 1)).astype(np.float32)
+    assert abs(orc.z_loss(l1) - np.mean(l1.astype(np.float64) ** 2)) < 1e-13
+
+
+def pin_z_loss_library(orc):
+    """scipy's logsumexp on random scores, including large ones."""
+    from scipy.special import logsumexp
+    r = _rng(22)
+    for T, E in ((5, 8), (17, 256), (3, 1000)):
+        logits = (r.standard_normal((T, E)) * 20).astype(np.float32)
+        want = np.mean(logsumexp(logits.astype(np.float64), axis=1) ** 2)
+        assert abs(orc.z_loss(logits) - want) < 1e-11 * want
+
+
+def pin_aux_topk_relations(orc):
+    """K = E selects every expert for every token, so P'_e = P_e and the top-K aux
+    equals the full aux (= 1, since the choice fractions are uniform); for K < E
+    P'_e <= P_e, so the top-K aux never exceeds the full aux."""
+    r = _rng(23)
+    T, E = 11, 5
+    probs = r.dirichlet(np.ones(E), size=T)
+    ids = np.tile(np.arange(E, dtype=np.int32), (T, 1))
+    counts = np.full(E, T, np.int32)
+    got = orc.aux_topk(counts, ids, probs)
+    assert abs(got - orc.aux_loss(counts, probs, E)) < 1e-14 and abs(got - 1.0) < 1e-14
+    for K in (1, 2, 3):
+        logits = r.standard_normal((T, E)).astype(np.float32)
+        ids, _, p = orc.route(logits, K)
+        cnt = np.bincount(ids.ravel(), minlength=E).astype(np.int32)
+        assert orc.aux_topk(cnt, ids, p) <= orc.aux_loss(cnt, p, K) + 1e-15
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -38,6 +38,13 @@ MUTANTS = [
     ("aux without the N factor", "return (double)E * total;", "return total;"),
     ("bias update sign", "bias[e] = bias[e] - alpha;", "bias[e] = bias[e] + alpha;"),
     ("bias update moves at target", "else if (load < T * K)", "else if (load <= T * K)"),
+    ("z-loss not squared", "total += lse * lse;", "total += lse;"),
+    ("z-loss without the max", "double lse = m + log(s);", "double lse = log(s);"),
+    ("z-loss not averaged", "return total / (double)T;", "return total;"),
+    ("top-K aux counts every expert", "if (ids[t * K + k] == e) chosen += probs[t * E + e];",
+     "chosen += probs[t * E + e] / (double)K;"),
+    ("top-K aux over slots", "sum_fp += frac * (chosen / (double)T);", "sum_fp += frac * (chosen / (double)(T * K));"),
+    ("top-K aux without the N factor", "return sum_fp * (double)E;", "return sum_fp;"),
 ]
 
 
