@@ -201,6 +201,23 @@ moe_status moe_aux_loss(const moe_problem* p, const int32_t* counts, const float
 moe_status moe_bias_update(const moe_problem* p, const int32_t* counts, float alpha,
                            float* bias, void* stream);
 
+/* Router regularisers: [NOTES] §3.2.
+ *   z_loss   = (1/T) sum_t (log sum_e exp(logits[t,e]))^2 over the router
+ *              scores as moe_route writes them (before the bias);
+ *   aux_topk = E sum_e f_e P'_e, the cheaper aux loss that counts only the
+ *              probabilities of the chosen experts: f_e = counts[e] / (T*K),
+ *              P'_e = (1/T) sum_t sum_k [topk_ids[t,k] == e] p[t,e] with
+ *              p = softmax over all E of logits + logit_bias.
+ *   logits [T,E] fp32, logit_bias [E] fp32 or NULL, topk_ids [T,K] int32,
+ *   counts [E] int32 (routed, before any capacity cut; may be NULL when
+ *   aux_topk is NULL); z_loss, aux_topk: one fp32 each on the device, either
+ *   may be NULL.  ws: moe_router_losses_workspace_size bytes.  The sums run
+ *   in a fixed order (run-to-run identical). */
+moe_status moe_router_losses_workspace_size(const moe_problem* p, size_t* bytes);
+moe_status moe_router_losses(const moe_problem* p, const float* logits, const float* logit_bias,
+                             const int32_t* topk_ids, const int32_t* counts, float* z_loss,
+                             float* aux_topk, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- timing hook (tracing, not part of the layer) -------------------------
  * Kernels of the library, by id, for moe_set_kernel_timer / moe_kernel_name. */
 enum {
@@ -215,7 +232,8 @@ enum {
     MOE_KERNEL_AUX = 8,
     MOE_KERNEL_BIAS_UPDATE = 9,
     MOE_KERNEL_FFN_PLAN = 10,
-    MOE_KERNEL_COUNT = 11
+    MOE_KERNEL_ROUTER_LOSSES = 11,
+    MOE_KERNEL_COUNT = 12
 };
 
 /* Name of kernel `kid` ("?" when out of range). */

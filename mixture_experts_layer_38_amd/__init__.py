@@ -22,7 +22,7 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 KERNEL_IDS = {
     "router": 0, "dispatch_count": 1, "dispatch_scan": 2, "dispatch_scatter": 3,
     "dispatch_gather": 4, "ffn_gate_up": 5, "ffn_down": 6, "combine": 7, "aux_loss": 8,
-    "bias_update": 9, "ffn_plan": 10,
+    "bias_update": 9, "ffn_plan": 10, "router_losses": 11,
 }
 
 
@@ -63,6 +63,8 @@ def _lib():
         "moe_dispatch_workspace_size": [P, ctypes.POINTER(sz)],
         "moe_expert_ffn_workspace_size": [P, ctypes.POINTER(sz)],
         "moe_workspace_size": [P, ctypes.POINTER(sz)],
+        "moe_router_losses_workspace_size": [P, ctypes.POINTER(sz)],
+        "moe_router_losses": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_route": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_dispatch": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_expert_ffn": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -142,6 +144,10 @@ def moe_expert_ffn_workspace_size(p: MoEProblem) -> int:
     return _size(_lib().moe_expert_ffn_workspace_size, p)
 
 
+def moe_router_losses_workspace_size(p: MoEProblem) -> int:
+    return _size(_lib().moe_router_losses_workspace_size, p)
+
+
 def moe_route(p, x, w_router, logit_bias, logits, probs, prob_sum, topk_ids, topk_w,
               ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -187,6 +193,13 @@ def moe_aux_loss(p, counts, prob_sum, aux, stream=None):
                                _stream(stream)), "moe_aux_loss")
 
 
+def moe_router_losses(p, logits, logit_bias, topk_ids, counts, z_loss, aux_topk, ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib().moe_router_losses(ctypes.byref(p), _ptr(logits), _ptr(logit_bias), _ptr(topk_ids),
+                                    _ptr(counts), _ptr(z_loss), _ptr(aux_topk), _ptr(ws), ws_bytes,
+                                    _stream(stream)), "moe_router_losses")
+
+
 def moe_bias_update(p, counts, alpha: float, bias, stream=None):
     _check(_lib().moe_bias_update(ctypes.byref(p), _ptr(counts), ctypes.c_float(alpha), _ptr(bias),
                                   _stream(stream)), "moe_bias_update")
@@ -218,6 +231,7 @@ __all__ = [
     "CONFIGS", "MoEConfig", "MoEError", "MoEProblem", "MoEDebugOut", "load", "problem", "problem_of",
     "moe_workspace_size", "moe_route_workspace_size", "moe_dispatch_workspace_size",
     "moe_expert_ffn_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-    "moe_forward", "moe_aux_loss", "moe_bias_update", "moe_set_kernel_timer",
+    "moe_forward", "moe_aux_loss", "moe_bias_update", "moe_router_losses",
+    "moe_router_losses_workspace_size", "moe_set_kernel_timer",
     "moe_kernel_timer_count",
 ]

@@ -51,6 +51,12 @@ hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* 
                       const int32_t* rowmap, const int32_t* offsets, const void* w1,
                       const void* w3, const void* w2, void* act, void* h, void* ws, hipStream_t s);
 
+// ---- router regularisers ----------------------------------------------------
+size_t router_losses_ws_bytes(int T, int E);
+hipError_t launch_router_losses(int T, int E, int K, const float* logits, const float* bias,
+                                const int32_t* ids, const int32_t* counts, float* z_loss,
+                                float* aux_topk, void* ws, hipStream_t s);
+
 // ---- combine / aux / bias --------------------------------------------------
 hipError_t launch_combine(int T, int K, int d, int dtype, const void* h,
                           const int32_t* assign_row, const float* w, void* y, hipStream_t s);

@@ -120,7 +120,8 @@ const char* moe_version(void) { return "moe-gfx950 0.1"; }
 const char* moe_kernel_name(int kid) {
     static const char* names[MOE_KERNEL_COUNT] = {
         "router", "dispatch_count", "dispatch_scan", "dispatch_scatter", "dispatch_gather",
-        "ffn_gate_up", "ffn_down", "combine", "aux_loss", "bias_update", "ffn_plan"};
+        "ffn_gate_up", "ffn_down", "combine", "aux_loss", "bias_update", "ffn_plan",
+        "router_losses"};
     return (kid >= 0 && kid < MOE_KERNEL_COUNT) ? names[kid] : "?";
 }
 
@@ -313,6 +314,31 @@ moe_status moe_aux_loss(const moe_problem* p, const int32_t* counts, const float
     if (!counts || !prob_sum || !aux) return MOE_ERR_INVALID_ARG;
     return hip_status(launch_aux(p->T, p->top_k, p->n_experts, counts, prob_sum, aux,
                                  (hipStream_t)stream));
+}
+
+moe_status moe_router_losses_workspace_size(const moe_problem* p, size_t* bytes) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = router_losses_ws_bytes(p->T, p->n_experts);
+    return MOE_OK;
+}
+
+moe_status moe_router_losses(const moe_problem* p, const float* logits, const float* logit_bias,
+                             const int32_t* topk_ids, const int32_t* counts, float* z_loss,
+                             float* aux_topk, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    REQUIRE(logits);
+    REQUIRE(topk_ids);
+    OPTIONAL(logit_bias);
+    if (!z_loss && !aux_topk) return MOE_ERR_INVALID_ARG;
+    if (aux_topk && !counts) return MOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < router_losses_ws_bytes(p->T, p->n_experts)) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_router_losses(p->T, p->n_experts, p->top_k, logits, logit_bias,
+                                           topk_ids, counts, z_loss, aux_topk, ws,
+                                           (hipStream_t)stream));
 }
 
 moe_status moe_bias_update(const moe_problem* p, const int32_t* counts, float alpha, float* bias,

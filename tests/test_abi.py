@@ -37,6 +37,7 @@ def test_status_strings_and_kernel_names():
     for s in range(6):
         assert lib.moe_status_string(s)
     assert lib.moe_kernel_name(5) == b"ffn_gate_up"
+    assert lib.moe_kernel_name(11) == b"router_losses"
     assert lib.moe_kernel_name(99) == b"?"
 
 
@@ -106,6 +107,20 @@ def test_step_calls_reject_bad_arguments():
     assert lib.moe_combine(P, A, A, A, None, None) == INVALID
     assert lib.moe_aux_loss(P, None, A, A, None) == INVALID
     assert lib.moe_bias_update(P, A, ctypes.c_float(1e-3), None, None) == INVALID
+
+
+def test_router_losses_rejects_bad_arguments():
+    lib = moe.load()
+    p = moe.problem(64, 128, 8, 2, 256, "bf16")
+    P = ctypes.byref(p)
+    ws = moe.moe_router_losses_workspace_size(p)
+    assert ws >= 4 * 9
+    # no output requested; aux without counts; workspace too small; misaligned scores
+    assert lib.moe_router_losses(P, A, None, A, A, None, None, A, ws, None) == INVALID
+    assert lib.moe_router_losses(P, A, None, A, None, None, A, A, ws, None) == INVALID
+    assert lib.moe_router_losses(P, A, None, A, A, A, A, A, ws - 1, None) == WORKSPACE
+    assert lib.moe_router_losses(P, MIS, None, A, A, A, A, A, ws, None) == ALIGN
+    assert lib.moe_router_losses(P, A, None, None, A, A, A, A, ws, None) == INVALID
 
 
 def test_timer_hook_bookkeeping():
