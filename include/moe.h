@@ -60,6 +60,8 @@ typedef enum {
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 
+enum { MOE_FLAG_BIAS_SELECT_ONLY = 1u, MOE_FLAG_COMBINE_MEAN = 2u };
+
 /* Shape and options of one layer call.
  *   T         tokens (rows of x), T >= 1, T * top_k < 2^30
  *   d_model   d, multiple of 8, <= 65536
@@ -71,7 +73,13 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
  *             in flat assignment order t*K + k ([NOTES] §3.1: a capacity
  *             factor cf gives capacity = floor(cf * T * K / E), computed by the
  *             caller)
- *   flags     reserved, must be 0 */
+ *   flags     0, or an OR of
+ *             MOE_FLAG_BIAS_SELECT_ONLY: the logit bias steers which experts
+ *               are chosen, while the probabilities and the weights come from
+ *               the softmax of the unbiased scores ([ENG] §1.2 read as a
+ *               routing-only bias; without the flag the bias enters both);
+ *             MOE_FLAG_COMBINE_MEAN: the K outputs are averaged without
+ *               weights, every routing weight is 1/K ([NOTES] §2.3). */
 typedef struct {
     int32_t T;
     int32_t d_model;
@@ -128,7 +136,8 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
  *              be NULL
  *   topk_ids   [T, K] int32: experts by (l' descending, index ascending);
  *              -0.0 and +0.0 compare equal
- *   topk_w     [T, K] fp32: p[id_k] / sum_j p[id_j] */
+ *   topk_w     [T, K] fp32: p[id_k] / sum_j p[id_j] (1/K with
+ *              MOE_FLAG_COMBINE_MEAN) */
 moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* logit_bias, float* logits, float* probs,
                      float* prob_sum, int32_t* topk_ids, float* topk_w,

@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_FLAG_BIAS_SELECT_ONLY, MOE_FLAG_COMBINE_MEAN = 1, 2
 
 KERNEL_IDS = {
     "router": 0, "dispatch_count": 1, "dispatch_scan": 2, "dispatch_scatter": 3,
@@ -113,9 +114,9 @@ def _check(status: int, where: str):
 
 
 def problem(T: int, d_model: int, n_experts: int, top_k: int, d_ff: int, dtype: str = "bf16",
-            capacity: int = -1) -> MoEProblem:
+            capacity: int = -1, flags: int = 0) -> MoEProblem:
     code = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}[dtype]
-    return MoEProblem(T, d_model, n_experts, top_k, d_ff, code, capacity, 0)
+    return MoEProblem(T, d_model, n_experts, top_k, d_ff, code, capacity, flags)
 
 
 def problem_of(cfg: MoEConfig, T: int | None = None) -> MoEProblem:

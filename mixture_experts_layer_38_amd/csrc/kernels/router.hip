@@ -30,15 +30,19 @@ constexpr int RT_THREADS = 256;
 constexpr int RG_KCH = 128;  // d chunk per gemm iteration
 
 // ---- route ---------------------------------------------------------------------
-// Route one token whose biased-or-not scores this lane holds for experts
-// lane + 64 j.  The wave computes it together.  psum[j] accumulates this
-// wave's probabilities of expert lane + 64 j.
+// Route one token whose scores this lane holds for experts lane + 64 j.  The
+// wave computes it together.  psum[j] accumulates this wave's probabilities of
+// expert lane + 64 j.  flags: MOE_FLAG_BIAS_SELECT_ONLY (the bias steers the
+// choice only; probabilities and weights come from the unbiased scores),
+// MOE_FLAG_COMBINE_MEAN (every weight is 1/K).
 template <int MAXV>
 __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int K, const float* bias,
-                                            float* probs_row, int32_t* ids_row, float* w_row,
-                                            float (&psum)[MAXV]) {
+                                            int flags, float* probs_row, int32_t* ids_row,
+                                            float* w_row, float (&psum)[MAXV]) {
     const int lane = lane_id();
-    float v[MAXV];
+    const bool sel_only = (flags & MOE_FLAG_BIAS_SELECT_ONLY) != 0;
+    float v[MAXV];  // selection keys: scores + bias
+    float u[MAXV];  // softmax inputs: the same, or the unbiased scores
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
@@ -46,9 +50,11 @@ __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int 
         if (e < E) {
             const float b = bias ? bias[e] : 0.0f;
             v[j] = lg[j] + b;  // one fp32 addition, round to nearest even
-            m = fmaxf(m, v[j]);
+            u[j] = sel_only ? lg[j] : v[j];
+            m = fmaxf(m, u[j]);
         } else {
             v[j] = -INFINITY;
+            u[j] = -INFINITY;
         }
     }
     m = wave_max(m);
@@ -57,7 +63,7 @@ __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int 
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
         const int e = lane + j * kWave;
-        ex[j] = (e < E) ? expf(v[j] - m) : 0.0f;
+        ex[j] = (e < E) ? expf(u[j] - m) : 0.0f;
         s += ex[j];
     }
     s = wave_sum(s);
@@ -101,7 +107,15 @@ __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int 
             }
         }
         if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-        const float ek = expf(bv - m);  // same value as ex[] of the winner
+        float uw = bv;  // softmax input of the winner
+        if (sel_only) {
+            float mine = 0.0f;
+#pragma unroll
+            for (int j = 0; j < MAXV; ++j)
+                if (j == bi / kWave) mine = u[j];
+            uw = __shfl(mine, bi & (kWave - 1));
+        }
+        const float ek = expf(uw - m);  // same value as ex[] of the winner
         sel_sum += ek;
         if (lane == k) {
             my_e = ek;
@@ -110,7 +124,7 @@ __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int 
     }
     if (lane < K) {
         ids_row[lane] = my_id;
-        w_row[lane] = my_e / sel_sum;
+        w_row[lane] = (flags & MOE_FLAG_COMBINE_MEAN) ? 1.0f / (float)K : my_e / sel_sum;
     }
 }
 
@@ -119,8 +133,9 @@ __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int 
 // there.  psum_part (optional) receives this block's per-expert probability sums.
 template <int MAXV>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(
-    int T, int E, int K, int nsplit, const float* __restrict__ src, float* __restrict__ logits_out,
-    const float* __restrict__ bias, float* __restrict__ probs, float* __restrict__ psum_part,
+    int T, int E, int K, int flags, int nsplit, const float* __restrict__ src,
+    float* __restrict__ logits_out, const float* __restrict__ bias, float* __restrict__ probs,
+    float* __restrict__ psum_part,
     int32_t* __restrict__ ids, float* __restrict__ w) {
     extern __shared__ float red[];  // [RT_THREADS / kWave][E]
     const int wave = threadIdx.x / kWave;
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
             }
             lg[j] = acc;
         }
-        route_token<MAXV>(lg, E, K, bias, probs ? probs + (size_t)t * E : nullptr,
+        route_token<MAXV>(lg, E, K, bias, flags, probs ? probs + (size_t)t * E : nullptr,
                           ids + (size_t)t * K, w + (size_t)t * K, psum);
     }
     if (psum_part) {
@@ -348,22 +363,22 @@ static RouterLayout router_layout(int T, int d, int E, int dtype) {
 size_t router_ws_bytes(int T, int d, int E, int dtype) { return router_layout(T, d, E, dtype).total; }
 
 template <int MAXV>
-static hipError_t launch_route_t(int T, int E, int K, int nsplit, const float* src, float* logits_out,
+static hipError_t launch_route_t(int T, int E, int K, int flags, int nsplit, const float* src, float* logits_out,
                                  const float* bias, float* probs, float* psum_part, int32_t* ids,
                                  float* w, hipStream_t s) {
     const int nblk = router_num_blocks(T, 0);
     MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER, s,
                      route_kernel<MAXV><<<nblk, RT_THREADS, (size_t)(RT_THREADS / kWave) * E * 4, s>>>(
-                         T, E, K, nsplit, src, logits_out, bias, probs, psum_part, ids, w));
+                         T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, ids, w));
     return hipGetLastError();
 }
 
-static hipError_t launch_route(int T, int E, int K, int nsplit, const float* src, float* logits_out,
+static hipError_t launch_route(int T, int E, int K, int flags, int nsplit, const float* src, float* logits_out,
                                const float* bias, float* probs, float* psum_part, int32_t* ids,
                                float* w, hipStream_t s) {
-    if (E <= 64) return launch_route_t<1>(T, E, K, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
-    if (E <= 256) return launch_route_t<4>(T, E, K, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
-    return launch_route_t<16>(T, E, K, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
+    if (E <= 64) return launch_route_t<1>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
+    if (E <= 256) return launch_route_t<4>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
+    return launch_route_t<16>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
 }
 
 template <int NEB>
@@ -373,7 +388,7 @@ static void launch_gemm_t(int T, int d, int E, int ns, const bf16* x, const bf16
     router_gemm_kernel<NEB><<<grid, 256, 0, s>>>(T, d, E, router_kspan(d, ns), x, wrt, out);
 }
 
-hipError_t launch_router(int T, int d, int E, int K, int dtype, const void* x,
+hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const void* x,
                          const void* w_router, const float* bias, float* logits, float* probs,
                          float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s) {
     const RouterLayout L = router_layout(T, d, E, dtype);
@@ -407,7 +422,7 @@ hipError_t launch_router(int T, int d, int E, int K, int dtype, const void* x,
             T, d, E, (const float*)x, (const float*)w_router, logits);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    err = launch_route(T, E, K, nsplit, src, logits_out, bias, probs, part, ids, w, s);
+    err = launch_route(T, E, K, flags, nsplit, src, logits_out, bias, probs, part, ids, w, s);
     if (err != hipSuccess || !prob_sum) return err;
     psum_reduce_kernel<<<(E + 3) / 4, 256, 0, s>>>(router_num_blocks(T, dtype), E, part, prob_sum);
     return hipGetLastError();

@@ -30,7 +30,7 @@ int router_num_blocks(int T, int dtype);
 // Workspace of the router: W_r^T and partial scores (bf16 scores from x) and
 // the per-block probability sums.
 size_t router_ws_bytes(int T, int d, int E, int dtype);
-hipError_t launch_router(int T, int d, int E, int K, int dtype, const void* x,
+hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const void* x,
                          const void* w_router, const float* bias, float* logits, float* probs,
                          float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s);
 

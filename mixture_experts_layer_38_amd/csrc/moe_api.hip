@@ -39,7 +39,7 @@ static moe_status check_problem(const moe_problem* p) {
     if (p->T <= 0 || p->d_model <= 0 || p->n_experts <= 0 || p->top_k <= 0 || p->d_ff <= 0)
         return MOE_ERR_INVALID_ARG;
     if (p->top_k > p->n_experts) return MOE_ERR_INVALID_ARG;
-    if (p->flags != 0) return MOE_ERR_INVALID_ARG;
+    if (p->flags & ~(uint32_t)(MOE_FLAG_BIAS_SELECT_ONLY | MOE_FLAG_COMBINE_MEAN)) return MOE_ERR_INVALID_ARG;
     if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->n_experts > 1024 || p->top_k > 32) return MOE_ERR_UNSUPPORTED;
     if (p->d_model % 8 != 0 || p->d_ff % 8 != 0) return MOE_ERR_UNSUPPORTED;
@@ -192,7 +192,7 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
             return MOE_ERR_WORKSPACE;
         if (!aligned16(ws)) return MOE_ERR_ALIGNMENT;
     }
-    return hip_status(launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype, x,
+    return hip_status(launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype, (int)p->flags, x,
                                     w_router, logit_bias, logits, probs, prob_sum, topk_ids,
                                     topk_w, ws, (hipStream_t)stream));
 }
@@ -290,7 +290,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     void* act = base + L.act;
     void* h = base + L.h;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t err = launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype, x, w_router,
+    hipError_t err = launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype, (int)p->flags, x, w_router,
                                    logit_bias, logits, D.probs, D.prob_sum, ids, w,
                                    base + L.route_ws, s);
     if (err != hipSuccess) return MOE_ERR_HIP;

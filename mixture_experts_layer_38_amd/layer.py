@@ -35,7 +35,7 @@ class MoELayer:
     """One MoE layer with its weights resident in HBM."""
 
     def __init__(self, T: int, d: int, E: int, K: int, F: int, dtype: str, w_router, w1, w3, w2,
-                 capacity: int = -1, device="cuda"):
+                 capacity: int = -1, device="cuda", flags: int = 0):
         import torch
         self.T, self.d, self.E, self.K, self.F = T, d, E, K, F
         self.dtype = dtype
@@ -43,16 +43,18 @@ class MoELayer:
         self.device = device
         self.w_router, self.w1, self.w3, self.w2 = w_router, w1, w3, w2
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.p: MoEProblem = problem(T, d, E, K, F, dtype, capacity)
+        self.flags = flags
+        self.p: MoEProblem = problem(T, d, E, K, F, dtype, capacity, flags)
         self.ws = torch.empty(moe_workspace_size(self.p), dtype=torch.uint8, device=device)
 
     @classmethod
-    def from_host(cls, cfg: MoEConfig, inputs: dict, device="cuda", T: int | None = None):
+    def from_host(cls, cfg: MoEConfig, inputs: dict, device="cuda", T: int | None = None,
+                  flags: int = 0):
         dt = cfg.dtype
         return cls(cfg.T if T is None else T, cfg.d, cfg.E, cfg.K, cfg.F, dt,
                    to_device(inputs["w_router"], dt, device), to_device(inputs["w1"], dt, device),
                    to_device(inputs["w3"], dt, device), to_device(inputs["w2"], dt, device),
-                   cfg.capacity, device)
+                   cfg.capacity, device, flags)
 
     def alloc_debug(self) -> dict:
         import torch

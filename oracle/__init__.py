@@ -83,7 +83,14 @@ class Oracle:
         return out
 
     def route(self, logits: np.ndarray, K: int, bias: np.ndarray | None = None,
-              want_probs: bool = True):
+              want_probs: bool = True, select_only: bool = False, mean: bool = False):
+        """Routing of fp32 scores (see oracle.h).  Two variants:
+        select_only: the bias decides which K experts are chosen, and the
+            weights and probabilities come from the softmax of the unbiased
+            scores (the other reading of the engineering page's §1.2, where
+            the balancing bias only steers the selection);
+        mean: the K outputs are averaged without weights (MoE notes §2.3,
+            third combine form), i.e. every weight is 1/K."""
         logits = np.ascontiguousarray(logits, np.float32)
         T, E = logits.shape
         if not (1 <= K <= E):
@@ -91,8 +98,14 @@ class Oracle:
         b = None if bias is None else np.ascontiguousarray(bias, np.float32)
         ids = np.empty((T, K), np.int32)
         w = np.empty((T, K), np.float64)
-        probs = np.empty((T, E), np.float64) if want_probs else None
+        probs = np.empty((T, E), np.float64) if (want_probs or select_only) else None
         self.lib.oracle_route(T, E, K, _p(logits), _p(b), _p(ids), _p(w), _p(probs))
+        if select_only:
+            _, _, probs = self.route(logits, K, None)
+            chosen = np.take_along_axis(probs, ids.astype(np.int64), axis=1)
+            w = chosen / chosen.sum(axis=1, keepdims=True)
+        if mean:
+            w = np.full((T, K), 1.0 / K)
         return ids, w, probs
 
     def dispatch(self, ids: np.ndarray, E: int, capacity: int = -1) -> dict:

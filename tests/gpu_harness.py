@@ -28,10 +28,11 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run_forward(cfg: MoEConfig, inp: dict, logit_bias: np.ndarray | None = None, repeat: int = 1):
+def run_forward(cfg: MoEConfig, inp: dict, logit_bias: np.ndarray | None = None, repeat: int = 1,
+                flags: int = 0):
     """moe_forward with every debug output; returns host arrays (and the layer)."""
     import torch
-    layer = MoELayer.from_host(cfg, inp)
+    layer = MoELayer.from_host(cfg, inp, flags=flags)
     x = to_device(inp["x"], cfg.dtype)
     lb = inp["logit_bias"] if logit_bias is None else logit_bias
     bias = None if lb is None else torch.from_numpy(np.ascontiguousarray(lb, np.float32)).cuda()
@@ -61,9 +62,10 @@ def check_logits(orc, inp, gpu_logits, tokens=None):
     return err
 
 
-def check_routing(orc, cfg: MoEConfig, out: dict, bias):
+def check_routing(orc, cfg: MoEConfig, out: dict, bias, flags: int = 0):
     """Bit-exact ids from the GPU's logits; weights within TOL_W; probabilities."""
-    ids, w, probs = orc.route(out["logits"], cfg.K, bias)
+    ids, w, probs = orc.route(out["logits"], cfg.K, bias, select_only=bool(flags & 1),
+                              mean=bool(flags & 2))
     bad = np.nonzero((ids != out["topk_ids"]).any(1))[0]
     assert len(bad) == 0, f"{len(bad)} tokens with different expert ids, first {bad[:5]}"
     dw = np.abs(out["topk_w"].astype(np.float64) - w).max()

@@ -474,4 +474,44 @@ def pin_aux_topk_relations(orc):
         assert orc.aux_topk(cnt, ids, p) <= orc.aux_loss(cnt, p, K) + 1e-15
 
 
+# --------------------------------------------------------------------------
+# routing variants (engineering page §1.2, notes §2.3)
+# --------------------------------------------------------------------------
+
+def pin_route_variants_hand(orc):
+    """Hand-worked token: bias in selection and weights, in selection only, and
+    the unweighted mean (values derived in the fixture)."""
+    g = _golden("route_variants_hand.json")
+    logits = np.array(g["logits"], np.float32)
+    bias = np.array(g["bias"], np.float32)
+    for key, kw in (("expect_w_both", {}), ("expect_w_select_only", {"select_only": True}),
+                    ("expect_w_mean", {"mean": True})):
+        ids, w, _ = orc.route(logits, g["K"], bias, **kw)
+        assert ids.tolist() == g["expect_ids"], (key, ids)
+        np.testing.assert_allclose(w, np.array(g[key]), rtol=0, atol=1e-15, err_msg=key)
+
+
+def pin_select_only_properties(orc):
+    """Selection-only bias: the chosen set is the biased top-K, the weights are
+    the unbiased softmax renormalised over it, and with a zero bias it reduces
+    to the plain router."""
+    r = _rng(24)
+    T, E, K = 40, 16, 3
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    bias = r.uniform(-2, 2, E).astype(np.float32)
+    ids_b, _, _ = orc.route(logits, K, bias)
+    ids, w, probs = orc.route(logits, K, bias, select_only=True)
+    assert np.array_equal(ids, ids_b)
+    _, _, p0 = orc.route(logits, K, None)
+    np.testing.assert_allclose(probs, p0, rtol=0, atol=0)
+    for t in range(T):
+        v = logits[t, ids[t]].astype(np.float64)
+        ev = np.exp(v - v.max())
+        np.testing.assert_allclose(w[t], ev / ev.sum(), rtol=1e-13, atol=0)
+    zero = np.zeros(E, np.float32)
+    a = orc.route(logits, K, zero, select_only=True)
+    b = orc.route(logits, K, zero)
+    assert np.array_equal(a[0], b[0]) and np.allclose(a[1], b[1], rtol=0, atol=1e-15)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -48,7 +48,8 @@ def _ws(p):
 @pytest.mark.parametrize("kw,status", [
     (dict(T=0), INVALID), (dict(T=-3), INVALID), (dict(top_k=9), INVALID), (dict(top_k=0), INVALID),
     (dict(n_experts=2000, top_k=2), UNSUPPORTED), (dict(d_model=100), UNSUPPORTED),
-    (dict(d_ff=1410), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED), (dict(flags=1), INVALID),
+    (dict(d_ff=1410), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED), (dict(flags=4), INVALID),
+    (dict(flags=3), OK),
     (dict(n_experts=64, top_k=33), UNSUPPORTED), (dict(T=1 << 29, top_k=2), UNSUPPORTED),
 ])
 def test_problem_checks(kw, status):

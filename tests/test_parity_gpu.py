@@ -37,19 +37,19 @@ def orc():
     return oracle.get()
 
 
-def _case(orc, cfg: MoEConfig, logit_bias=None, sample=None):
+def _case(orc, cfg: MoEConfig, logit_bias=None, sample=None, flags: int = 0):
     say(f"[case] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} K={cfg.K} F={cfg.F} {cfg.dtype} "
-        f"C={cfg.capacity}")
+        f"C={cfg.capacity} flags={flags}")
     inp = datagen.make_inputs(cfg)
     bias = inp["logit_bias"] if logit_bias is None else logit_bias
-    out, _ = run_forward(cfg, inp, bias)
+    out, _ = run_forward(cfg, inp, bias, flags=flags)
     say("   ", load_summary(cfg, out))
     tokens = None
     if sample is not None:
         rng = np.random.default_rng(1234)
         tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, sample, replace=False)]))
     check_logits(orc, inp, out["logits"], tokens)
-    ids, w, probs = check_routing(orc, cfg, out, bias)
+    ids, w, probs = check_routing(orc, cfg, out, bias, flags)
     ref = check_dispatch(orc, cfg, ids, out, cfg.capacity)
     err = check_output(orc, cfg, inp, ids, w, ref["assign_row"], out["y"], tokens)
     say(f"    output error {err:.3e}")
@@ -120,3 +120,10 @@ def test_aux_and_bias_reduced(orc):
     cfg = REDUCED["capacity_t2048"]
     inp, out, ids, w, probs = _case(orc, cfg)
     _check_aux_and_bias(orc, cfg, out, probs)
+
+
+@pytest.mark.parametrize("name,flags", [("dsv3_t256", 1), ("capacity_t2048", 2), ("prefill_t600_ragged", 3),
+                                        ("tiny_fp32", 1), ("decode_d512", 2)])
+def test_forward_routing_variants(orc, name, flags):
+    """Bias for selection only (flag 1), unweighted mean combine (flag 2), both."""
+    _case(orc, REDUCED[name], flags=flags)

@@ -30,13 +30,15 @@ def _empty(shape, dtype):
     return torch.empty(shape, dtype=dtype, device="cuda")
 
 
-@pytest.mark.parametrize("E,K,with_bias", [(8, 2, False), (8, 1, True), (64, 2, True),
-                                            (256, 8, True), (5, 5, False), (1000, 7, True)])
-def test_route_given_logits_with_ties(orc, E, K, with_bias):
+@pytest.mark.parametrize("E,K,with_bias,flags", [(8, 2, False, 0), (8, 1, True, 0), (64, 2, True, 0),
+                                                  (256, 8, True, 0), (5, 5, False, 0), (1000, 7, True, 0),
+                                                  (64, 2, True, 1), (256, 8, True, 1), (1000, 7, True, 3),
+                                                  (8, 2, True, 2)])
+def test_route_given_logits_with_ties(orc, E, K, with_bias, flags):
     """x = NULL mode: the GPU routes logits chosen by the test, full of exact
     ties and signed zeros; ids must match the oracle bit for bit."""
     import torch
-    say(f"[case] route ties E={E} K={K} bias={with_bias}")
+    say(f"[case] route ties E={E} K={K} bias={with_bias} flags={flags}")
     rng = np.random.default_rng(E * 100 + K)
     T = 333
     vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0, 2.0], np.float32)
@@ -44,7 +46,7 @@ def test_route_given_logits_with_ties(orc, E, K, with_bias):
     bias = None
     if with_bias:
         bias = rng.choice(np.array([-0.0, 0.0, 0.5, -0.5], np.float32), size=E).astype(np.float32)
-    p = moe.problem(T, 64, E, K, 64, "bf16")
+    p = moe.problem(T, 64, E, K, 64, "bf16", flags=flags)
     lg = _t(logits)
     ids = _empty((T, K), torch.int32)
     w = _empty((T, K), torch.float32)
@@ -53,7 +55,7 @@ def test_route_given_logits_with_ties(orc, E, K, with_bias):
     ws = _empty((moe.moe_route_workspace_size(p),), torch.uint8)
     moe.moe_route(p, None, None, None if bias is None else _t(bias), lg, probs, psum, ids, w, ws)
     torch.cuda.synchronize()
-    ids_ref, w_ref, p_ref = orc.route(logits, K, bias)
+    ids_ref, w_ref, p_ref = orc.route(logits, K, bias, select_only=bool(flags & 1), mean=bool(flags & 2))
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
     assert np.abs(w.cpu().numpy() - w_ref).max() <= TOL_W
     assert np.abs(probs.cpu().numpy() - p_ref).max() <= TOL_W
