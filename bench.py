@@ -138,6 +138,30 @@ def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use
     return wall, float(np.mean(kern_ms)) if kern_ms else float("nan"), counts, kept
 
 
+def time_chunked(cfg, layer, x, bias, chunk: int, steps: int):
+    """The same prefill batch through moe_forward_chunked (chunks of `chunk`
+    tokens, one workspace of one chunk's size): step time and workspace bytes
+    against the unchunked layer."""
+    import torch
+    import mixture_experts_layer_38_amd as moe
+    p = layer.p
+    ws_bytes = moe.moe_forward_chunked_workspace_size(p, chunk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((cfg.T, cfg.d), dtype=layer.torch_dtype, device="cuda")
+
+    def run():
+        moe.moe_forward_chunked(p, chunk, x, layer.w_router, layer.w1, layer.w3, layer.w2, bias, y, ws)
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    return {"chunk_tokens": chunk, "ms_per_step": ms, "value": cfg.T / (ms * 1e-3), "unit": "tokens/s",
+            "workspace_bytes": ws_bytes, "workspace_bytes_unchunked": moe.moe_workspace_size(p)}
+
+
 def cpu_baseline(cfg, inp, min_seconds: float = 10.0, max_reps: int = 200):
     """The CPU oracle (fp64, OpenMP on this host's cores) on the same workload:
     whole forward passes of the first min(T, 32) tokens (routing, grouping,
@@ -170,6 +194,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_decode")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-chunk", type=int, default=2048)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every pass eagerly instead of replaying a HIP graph")
@@ -239,6 +264,7 @@ def main():
                          "traffic": load_traffic(pcfg.name, "ffn_gate_up", "prefill"), "kernel_ms": pk_ms},
             "layer_mfma_frac": plf / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
             "counts": pcounts.tolist(),
+            "chunked": time_chunked(pcfg, player, px, pb, args.prefill_chunk, args.prefill_steps),
         }
         del player, px
     if not args.no_cpu:

@@ -197,6 +197,22 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
                        const float* logit_bias, void* y, const moe_debug_out* dbg,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Chunked forward: [NOTES] §4.3 (chunked MoE for prefill: run the token block
+ * in chunks to cap peak memory).  The same layer as moe_forward, run over
+ * tokens [t0, t0 + chunk_tokens) one chunk after another on `stream`, with a
+ * workspace of moe_forward_chunked_workspace_size bytes (the size for one
+ * chunk).  Each token's routing and output are defined as in moe_forward.
+ * Capacity must be unlimited (capacity < 0; a per-batch cap does not split
+ * into chunks: MOE_ERR_UNSUPPORTED otherwise), and of `dbg` only the
+ * per-token fields (logits, probs, topk_ids, topk_w) may be set. */
+moe_status moe_forward_chunked_workspace_size(const moe_problem* p, int32_t chunk_tokens,
+                                              size_t* bytes);
+moe_status moe_forward_chunked(const moe_problem* p, int32_t chunk_tokens, const void* x,
+                               const void* w_router, const void* w1, const void* w3,
+                               const void* w2, const float* logit_bias, void* y,
+                               const moe_debug_out* dbg, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Aux loss: [NOTES] §1.2, aux = E * sum_e f_e P_e with f_e = counts[e]/(T*K)
  * (counts before any capacity drop) and P_e = prob_sum[e]/T.
  *   counts [E] int32, prob_sum [E] fp32, aux: one fp32 (device). */

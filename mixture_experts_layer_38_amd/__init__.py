@@ -65,6 +65,9 @@ def _lib():
         "moe_expert_ffn_workspace_size": [P, ctypes.POINTER(sz)],
         "moe_workspace_size": [P, ctypes.POINTER(sz)],
         "moe_router_losses_workspace_size": [P, ctypes.POINTER(sz)],
+        "moe_forward_chunked_workspace_size": [P, ctypes.c_int32, ctypes.POINTER(sz)],
+        "moe_forward_chunked": [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp,
+                                ctypes.POINTER(MoEDebugOut), vp, sz, vp],
         "moe_router_losses": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_route": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_dispatch": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -189,6 +192,25 @@ def moe_forward(p, x, w_router, w1, w3, w2, logit_bias, y, ws, dbg: dict | None 
                               _stream(stream)), "moe_forward")
 
 
+def moe_forward_chunked_workspace_size(p: MoEProblem, chunk_tokens: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib().moe_forward_chunked_workspace_size(ctypes.byref(p), chunk_tokens, ctypes.byref(out)),
+           "moe_forward_chunked_workspace_size")
+    return out.value
+
+
+def moe_forward_chunked(p, chunk_tokens: int, x, w_router, w1, w3, w2, logit_bias, y, ws,
+                        dbg: dict | None = None, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    d = None
+    if dbg:
+        d = MoEDebugOut(**{k: _ptr(v) for k, v in dbg.items()})
+    _check(_lib().moe_forward_chunked(ctypes.byref(p), chunk_tokens, _ptr(x), _ptr(w_router), _ptr(w1),
+                                      _ptr(w3), _ptr(w2), _ptr(logit_bias), _ptr(y),
+                                      ctypes.byref(d) if d is not None else None, _ptr(ws), ws_bytes,
+                                      _stream(stream)), "moe_forward_chunked")
+
+
 def moe_aux_loss(p, counts, prob_sum, aux, stream=None):
     _check(_lib().moe_aux_loss(ctypes.byref(p), _ptr(counts), _ptr(prob_sum), _ptr(aux),
                                _stream(stream)), "moe_aux_loss")
@@ -232,7 +254,7 @@ __all__ = [
     "CONFIGS", "MoEConfig", "MoEError", "MoEProblem", "MoEDebugOut", "load", "problem", "problem_of",
     "moe_workspace_size", "moe_route_workspace_size", "moe_dispatch_workspace_size",
     "moe_expert_ffn_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-    "moe_forward", "moe_aux_loss", "moe_bias_update", "moe_router_losses",
+    "moe_forward", "moe_forward_chunked", "moe_forward_chunked_workspace_size", "moe_aux_loss", "moe_bias_update", "moe_router_losses",
     "moe_router_losses_workspace_size", "moe_set_kernel_timer",
     "moe_kernel_timer_count",
 ]

@@ -97,6 +97,69 @@ static ForwardLayout forward_layout(const moe_problem* p) {
     return L;
 }
 
+// Workspace of the chunked forward: the larger of the layouts of the two chunk
+// sizes it uses (a full chunk and the remainder; some scratch regions are not
+// monotone in T).
+static size_t chunked_ws_bytes(const moe_problem* p, int chunk_tokens) {
+    moe_problem c = *p;
+    c.T = chunk_tokens < p->T ? chunk_tokens : p->T;
+    size_t total = forward_layout(&c).total;
+    const int rem = p->T % c.T;
+    if (rem) {
+        c.T = rem;
+        const size_t r = forward_layout(&c).total;
+        if (r > total) total = r;
+    }
+    return total;
+}
+
+static moe_status check_debug(const moe_debug_out& D) {
+    OPTIONAL(D.logits);
+    OPTIONAL(D.probs);
+    OPTIONAL(D.prob_sum);
+    OPTIONAL(D.topk_ids);
+    OPTIONAL(D.topk_w);
+    OPTIONAL(D.counts);
+    OPTIONAL(D.kept);
+    OPTIONAL(D.offsets);
+    OPTIONAL(D.assign_row);
+    OPTIONAL(D.row_assign);
+    return MOE_OK;
+}
+
+// The launches of one forward pass over the problem's T tokens, with the
+// workspace carved by L (arguments already checked).
+static moe_status forward_launch(const moe_problem* p, const ForwardLayout& L, const void* x,
+                                 const void* w_router, const void* w1, const void* w3,
+                                 const void* w2, const float* logit_bias, void* y,
+                                 const moe_debug_out& D, char* base, hipStream_t s) {
+    float* logits = D.logits ? D.logits : (float*)(base + L.logits);
+    int32_t* ids = D.topk_ids ? D.topk_ids : (int32_t*)(base + L.ids);
+    float* w = D.topk_w ? D.topk_w : (float*)(base + L.w);
+    int32_t* counts = D.counts ? D.counts : (int32_t*)(base + L.counts);
+    int32_t* kept = D.kept ? D.kept : (int32_t*)(base + L.kept);
+    int32_t* offsets = D.offsets ? D.offsets : (int32_t*)(base + L.offsets);
+    int32_t* assign_row = D.assign_row ? D.assign_row : (int32_t*)(base + L.assign_row);
+    int32_t* row_assign = D.row_assign ? D.row_assign : (int32_t*)(base + L.row_assign);
+    void* act = base + L.act;
+    void* h = base + L.h;
+    hipError_t err = launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype,
+                                   (int)p->flags, x, w_router, logit_bias, logits, D.probs,
+                                   D.prob_sum, ids, w, base + L.route_ws, s);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    // The grouped token rows are never materialised: the first GEMM reads
+    // token row_assign[r] / K for its grouped row r.
+    err = launch_dispatch(p->T, p->top_k, p->n_experts, p->d_model, p->dtype, p->capacity, ids,
+                          nullptr, counts, kept, offsets, assign_row, row_assign, nullptr,
+                          base + L.disp_ws, s);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    err = launch_ffn(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype, x, row_assign,
+                     offsets, w1, w3, w2, act, h, base + L.ffn_ws, s);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    err = launch_combine(p->T, p->top_k, p->d_model, p->dtype, h, assign_row, w, y, s);
+    return hip_status(err);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -265,46 +328,65 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     moe_debug_out none;
     memset(&none, 0, sizeof none);
     const moe_debug_out& D = dbg ? *dbg : none;
-    OPTIONAL(D.logits);
-    OPTIONAL(D.probs);
-    OPTIONAL(D.prob_sum);
-    OPTIONAL(D.topk_ids);
-    OPTIONAL(D.topk_w);
-    OPTIONAL(D.counts);
-    OPTIONAL(D.kept);
-    OPTIONAL(D.offsets);
-    OPTIONAL(D.assign_row);
-    OPTIONAL(D.row_assign);
+    if ((st = check_debug(D)) != MOE_OK) return st;
     const ForwardLayout L = forward_layout(p);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGNMENT;
-    char* base = (char*)ws;
-    float* logits = D.logits ? D.logits : (float*)(base + L.logits);
-    int32_t* ids = D.topk_ids ? D.topk_ids : (int32_t*)(base + L.ids);
-    float* w = D.topk_w ? D.topk_w : (float*)(base + L.w);
-    int32_t* counts = D.counts ? D.counts : (int32_t*)(base + L.counts);
-    int32_t* kept = D.kept ? D.kept : (int32_t*)(base + L.kept);
-    int32_t* offsets = D.offsets ? D.offsets : (int32_t*)(base + L.offsets);
-    int32_t* assign_row = D.assign_row ? D.assign_row : (int32_t*)(base + L.assign_row);
-    int32_t* row_assign = D.row_assign ? D.row_assign : (int32_t*)(base + L.row_assign);
-    void* act = base + L.act;
-    void* h = base + L.h;
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t err = launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype, (int)p->flags, x, w_router,
-                                   logit_bias, logits, D.probs, D.prob_sum, ids, w,
-                                   base + L.route_ws, s);
-    if (err != hipSuccess) return MOE_ERR_HIP;
-    // The grouped token rows are never materialised: the first GEMM reads
-    // token row_assign[r] / K for its grouped row r.
-    err = launch_dispatch(p->T, p->top_k, p->n_experts, p->d_model, p->dtype, p->capacity, ids,
-                          nullptr, counts, kept, offsets, assign_row, row_assign, nullptr,
-                          base + L.disp_ws, s);
-    if (err != hipSuccess) return MOE_ERR_HIP;
-    err = launch_ffn(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype, x, row_assign,
-                     offsets, w1, w3, w2, act, h, base + L.ffn_ws, s);
-    if (err != hipSuccess) return MOE_ERR_HIP;
-    err = launch_combine(p->T, p->top_k, p->d_model, p->dtype, h, assign_row, w, y, s);
-    return hip_status(err);
+    return forward_launch(p, L, x, w_router, w1, w3, w2, logit_bias, y, D, (char*)ws,
+                          (hipStream_t)stream);
+}
+
+moe_status moe_forward_chunked_workspace_size(const moe_problem* p, int32_t chunk_tokens,
+                                              size_t* bytes) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!bytes || chunk_tokens <= 0) return MOE_ERR_INVALID_ARG;
+    *bytes = chunked_ws_bytes(p, chunk_tokens);
+    return MOE_OK;
+}
+
+moe_status moe_forward_chunked(const moe_problem* p, int32_t chunk_tokens, const void* x,
+                               const void* w_router, const void* w1, const void* w3,
+                               const void* w2, const float* logit_bias, void* y,
+                               const moe_debug_out* dbg, void* ws, size_t ws_bytes,
+                               void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (chunk_tokens <= 0) return MOE_ERR_INVALID_ARG;
+    if (p->capacity >= 0) return MOE_ERR_UNSUPPORTED;  // a per-batch cap does not split into chunks
+    REQUIRE(x);
+    REQUIRE(w_router);
+    REQUIRE(w1);
+    REQUIRE(w3);
+    REQUIRE(w2);
+    REQUIRE(y);
+    OPTIONAL(logit_bias);
+    moe_debug_out none;
+    memset(&none, 0, sizeof none);
+    const moe_debug_out& D = dbg ? *dbg : none;
+    if ((st = check_debug(D)) != MOE_OK) return st;
+    if (D.prob_sum || D.counts || D.kept || D.offsets || D.assign_row || D.row_assign)
+        return MOE_ERR_INVALID_ARG;  // only the per-token outputs are defined across chunks
+    const int chunk = chunk_tokens < p->T ? chunk_tokens : p->T;
+    moe_problem c = *p;
+    if (!ws || ws_bytes < chunked_ws_bytes(p, chunk)) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGNMENT;
+    const size_t es = elem_bytes(p);
+    const size_t d = p->d_model, E = p->n_experts, K = p->top_k;
+    for (int t0 = 0; t0 < p->T; t0 += chunk) {
+        c.T = (p->T - t0) < chunk ? (p->T - t0) : chunk;
+        const ForwardLayout L = forward_layout(&c);  // within chunked_ws_bytes by construction
+        moe_debug_out Dc = D;
+        if (D.logits) Dc.logits = D.logits + (size_t)t0 * E;
+        if (D.probs) Dc.probs = D.probs + (size_t)t0 * E;
+        if (D.topk_ids) Dc.topk_ids = D.topk_ids + (size_t)t0 * K;
+        if (D.topk_w) Dc.topk_w = D.topk_w + (size_t)t0 * K;
+        st = forward_launch(&c, L, (const char*)x + (size_t)t0 * d * es, w_router, w1, w3, w2,
+                            logit_bias, (char*)y + (size_t)t0 * d * es, Dc, (char*)ws,
+                            (hipStream_t)stream);
+        if (st != MOE_OK) return st;
+    }
+    return MOE_OK;
 }
 
 moe_status moe_aux_loss(const moe_problem* p, const int32_t* counts, const float* prob_sum,

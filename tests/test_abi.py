@@ -138,3 +138,20 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "libmoe.so"))
     with pytest.raises(RuntimeError, match="missing"):
         moe.load()
+
+
+def test_chunked_forward_checks():
+    lib = moe.load()
+    p = moe.problem(1000, 128, 8, 2, 256, "bf16")
+    P = ctypes.byref(p)
+    ws = moe.moe_forward_chunked_workspace_size(p, 256)
+    assert 0 < ws < moe.moe_workspace_size(p)
+    assert moe.moe_forward_chunked_workspace_size(p, 5000) == moe.moe_workspace_size(p)
+    # capacity is a per-batch rule: refused
+    pc = moe.problem(1000, 128, 8, 2, 256, "bf16", capacity=100)
+    assert lib.moe_forward_chunked(ctypes.byref(pc), 256, A, A, A, A, A, None, A, None, A, ws, None) == UNSUPPORTED
+    # bad chunk, small workspace, per-batch debug output
+    assert lib.moe_forward_chunked(P, 0, A, A, A, A, A, None, A, None, A, ws, None) == INVALID
+    assert lib.moe_forward_chunked(P, 256, A, A, A, A, A, None, A, None, A, ws - 1, None) == WORKSPACE
+    dbg = moe.MoEDebugOut(counts=A)
+    assert lib.moe_forward_chunked(P, 256, A, A, A, A, A, None, A, ctypes.byref(dbg), A, ws, None) == INVALID

@@ -1,0 +1,54 @@
+"""Chunked forward (moe_forward_chunked) against the oracle: the routing of
+every token bit-exact (the oracle routes the GPU's own scores) and the output
+within the bf16 tolerance, for chunks that divide T, leave a remainder, are
+one token, or exceed T."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import mixture_experts_layer_38_amd as moe
+from mixture_experts_layer_38_amd import datagen
+from mixture_experts_layer_38_amd.configs import CONFIGS, scaled
+from mixture_experts_layer_38_amd.layer import MoELayer, to_device, to_host
+from tests.gpu_harness import TOL_W, check_output, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+@pytest.mark.parametrize("cfg,chunk", [
+    (scaled(CONFIGS["mixtral_prefill"], T=3000, d=256, F=512), 1024),
+    (scaled(CONFIGS["mixtral_prefill"], T=3000, d=256, F=512), 700),
+    (scaled(CONFIGS["dsv3_routed"], T=600, d=256, F=256), 128),
+    (scaled(CONFIGS["mixtral_decode"], T=40, d=256, F=512), 1),
+    (scaled(CONFIGS["mixtral_decode"], T=40, d=256, F=512), 4096),
+])
+def test_chunked_forward(orc, cfg, chunk):
+    import torch
+    say(f"[case] chunked T={cfg.T} E={cfg.E} K={cfg.K} chunk={chunk}")
+    inp = datagen.make_inputs(cfg)
+    layer = MoELayer.from_host(cfg, inp)
+    x = to_device(inp["x"], cfg.dtype)
+    bias = None if inp["logit_bias"] is None else torch.from_numpy(inp["logit_bias"]).cuda()
+    p = moe.problem_of(cfg)
+    ws = torch.empty(moe.moe_forward_chunked_workspace_size(p, chunk), dtype=torch.uint8, device="cuda")
+    y = torch.empty((cfg.T, cfg.d), dtype=layer.torch_dtype, device="cuda")
+    dbg = {"logits": torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda"),
+           "topk_ids": torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda"),
+           "topk_w": torch.empty((cfg.T, cfg.K), dtype=torch.float32, device="cuda")}
+    moe.moe_forward_chunked(p, chunk, x, layer.w_router, layer.w1, layer.w3, layer.w2, bias, y, ws, dbg)
+    torch.cuda.synchronize()
+    logits = dbg["logits"].cpu().numpy()
+    ids, w, _ = orc.route(logits, cfg.K, inp["logit_bias"])
+    assert np.array_equal(ids, dbg["topk_ids"].cpu().numpy())
+    assert np.abs(dbg["topk_w"].cpu().numpy() - w).max() <= TOL_W
+    ref = orc.dispatch(ids, cfg.E, -1)
+    err = check_output(orc, cfg, inp, ids, w, ref["assign_row"], to_host(y, cfg.dtype))
+    say(f"    output error {err:.3e}; workspace {ws.numel() / 2**20:.1f} MiB vs "
+        f"{moe.moe_workspace_size(p) / 2**20:.1f} MiB unchunked")
