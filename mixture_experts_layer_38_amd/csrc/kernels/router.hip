@@ -321,11 +321,12 @@ static int router_neb(int E) {
 }
 
 // Slices of d for the score GEMM: enough waves to stream x, each slice a
-// multiple of the chunk width, and at most 8 MB of partial scores.
+// multiple of the chunk width, at most 8 slices and at most 8 MB of partial
+// scores.
 static int router_splits(int T, int d, int E) {
     const int neb = router_neb(E);
     const long waves = (long)((T + 15) / 16) * ((E + 16 * neb - 1) / (16 * neb));
-    const int max_split = max(1, d / RG_KCH);
+    const int max_split = max(1, min(8, d / RG_KCH));  // the route kernel sums the slices in one batch
     int ns = 1;
     while (ns * 2 <= max_split && waves * ns < 4096 &&
            (size_t)(ns * 2) * T * E * sizeof(float) <= ((size_t)8 << 20))
