@@ -29,6 +29,8 @@ REDUCED = {
     "decode_t64_e4": scaled(C["mixtral_decode"], T=64, d=256, E=4, F=520),
     "one_token": scaled(C["mixtral_prefill"], T=1, d=256, F=512),
     "k_equals_e": scaled(C["mixtral_decode"], T=40, d=128, E=4, K=4, F=256),
+    "top1_decode": scaled(C["mixtral_decode"], T=48, d=512, K=1, F=768),
+    "top1_prefill": scaled(C["mixtral_prefill"], T=900, d=320, K=1, F=384),
 }
 
 
