@@ -129,7 +129,10 @@ void ffn_prefill_kernel(
     // Loads: a stage is BM/8 A and 32 B wave instructions of 8 rows x 128
     // bytes; wave w issues rows [8 (w + 4 j), +8) of each.  Lane p fills slot
     // p % 8 of tile row p / 8 of its instruction, fetching the chunk that the
-    // swizzle puts there.
+    // swizzle puts there.  Tile rows past the expert's last row all read that
+    // last row (one line per stage, which the cache merges), so a partly
+    // filled tile asks L2 for little more than its real rows; every wave still
+    // issues the same number of loads on every stage.
     const int lr = lane >> 3;
     const int ls = lane & 7;
     const bf16* a_src[NJA];
@@ -137,7 +140,7 @@ void ffn_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < NJA; ++j) {
         const int tr = 8 * (wave + 4 * j) + lr;
-        const int r = src_row(rowmap, topk, min(row0 + tr, n_rows - 1));
+        const int r = src_row(rowmap, topk, min(row0 + tr, row_end - 1));
         a_src[j] = A + (size_t)r * K + (ls ^ pf_swz(tr)) * 8;
     }
 #pragma unroll
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(PG_THREADS) void ffn_prefill_generic_kernel(
     const bf16* b_src[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int r = src_row(rowmap, topk, min(row0 + lr + 64 * j, n_rows - 1));
+        const int r = src_row(rowmap, topk, min(row0 + lr + 64 * j, row_end - 1));
         a_src[j] = A + (size_t)r * K + lc;
         const int br = lr + 64 * j;  // weight row inside the tile
         if (GATED) {
