@@ -225,17 +225,30 @@ void ffn_prefill_kernel(
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * NTB - (4 + NTB), 0);
     };
+    // After the barrier: the last quarter's MFMAs, the loads of the next
+    // stage and the reads of the next stage's first quarter, one of each in
+    // turn, so no wave stalls on a burst of loads with its MFMAs waiting.
+    auto interleave_loads = [&]() {
+        constexpr int NM = 4 * NTB, NR = 4 + NTB;
+        constexpr int NI = NM > NLD ? NM : NLD;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
     // Stage kt lives in slot kt % NSLOT and is multiplied in four 16-wide
     // quarters; the LDS reads of each quarter overlap the MFMAs of the quarter
     // before.  After the third quarter's MFMAs: wait until this wave's reads
     // of slot kt % NSLOT are done and its loads of stage kt + 1 have landed
     // (the loads of later stages may still be in flight); a barrier then makes
     // stage kt + 1 visible to every wave and tells every wave that slot
-    // kt % NSLOT is free, and the loads of stage kt + NSLOT go there; the first
-    // quarter of stage kt + 1 is read during the last quarter's MFMAs.  Every
-    // step issues the same loads and reads (clamped to the last stage at the
-    // end, into slots no later step reads), so the counts of loads in flight
-    // are the same on every path.
+    // kt % NSLOT is free, and the loads of stage kt + NSLOT go there, spread
+    // over the last quarter's MFMAs together with the reads of the first
+    // quarter of stage kt + 1.  Every step issues the same loads and reads
+    // (clamped to the last stage at the end, into slots no later step reads),
+    // so the counts of loads in flight are the same on every path.
     Frags fa, fb;
     auto step = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB) {
         read(cA, cB, 1, fb);
@@ -255,10 +268,9 @@ void ffn_prefill_kernel(
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         issue(kt + NSLOT, cA, cB);
-        __builtin_amdgcn_sched_barrier(0);
         read(nA, nB, 0, fa);
         mma(fb);
-        interleave();
+        interleave_loads();
         __builtin_amdgcn_sched_barrier(0);
     };
     issue(0, sA0, sB0);
