@@ -30,6 +30,8 @@
 // expert in groups of PF_GM row tiles (row tile fastest inside a group), and
 // XCD x takes the x-th contiguous eighth of that list, so the tiles that run
 // together on one XCD share their token rows and weight rows in its L2.
+#include <type_traits>
+
 #include "../device_common.h"
 #include "../launch.h"
 
@@ -103,9 +105,14 @@ void ffn_prefill_kernel(
     constexpr int NJA = BM / 32;        // A load instructions per wave per stage
     constexpr int NJB = PF_BN / 32;     // B load instructions per wave per stage
     constexpr int NLD = NJA + NJB;      // loads per wave per stage
-    static_assert(NSLOT >= 2 && NSLOT <= 3, "two or three slots");
-    __shared__ __align__(1024) bf16 sA0[SA], sA1[SA], sA2[NSLOT > 2 ? SA : 1];
-    __shared__ __align__(1024) bf16 sB0[SB], sB1[SB], sB2[NSLOT > 2 ? SB : 1];
+    static_assert(NSLOT == 2 || NSLOT == 3 || (NSLOT == 5 && SA == SB), "slot scheme");
+    // NSLOT 2 or 3: that many whole stages (an A and a B slot each).  NSLOT 5:
+    // five half-stage units of 32 KB (all 160 KB of the LDS) that the A and B
+    // halves of consecutive stages take in turn.
+    constexpr bool HALF = NSLOT == 5;
+    __shared__ __align__(1024) bf16 sA0[SA], sA1[SA], sA2[NSLOT == 3 ? SA : 1];
+    __shared__ __align__(1024) bf16 sB0[SB], sB1[SB], sB2[NSLOT == 3 ? SB : 1];
+    __shared__ __align__(1024) bf16 sU4[HALF ? SB : 1];
     const int n_mt = *mt_count;
     const int tiles = n_mt * n_nt;
     const int per_xcd = (tiles + PF_XCD - 1) / PF_XCD;
@@ -161,18 +168,25 @@ void ffn_prefill_kernel(
         }
     }
     const int nk = K / PF_BK;
-    auto issue = [&](int kt, bf16* dA, bf16* dB) {
+    auto issue_a = [&](int kt, bf16* dA) {
         const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
         for (int j = 0; j < NJA; ++j)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[j] + ko),
                                              (__attribute__((address_space(3))) void*)(dA + 8 * (wave + 4 * j) * PF_BK),
                                              16, 0, 0);
+    };
+    auto issue_b = [&](int kt, bf16* dB) {
+        const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
         for (int j = 0; j < NJB; ++j)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b_src[j] + ko),
                                              (__attribute__((address_space(3))) void*)(dB + 8 * (wave + 4 * j) * PF_BK),
                                              16, 0, 0);
+    };
+    auto issue = [&](int kt, bf16* dA, bf16* dB) {
+        issue_a(kt, dA);
+        issue_b(kt, dB);
     };
 
     const int wm = wave & 1;   // token half of the tile (BM / 2 rows)
@@ -216,52 +230,65 @@ void ffn_prefill_kernel(
     };
     // Interleave: one MFMA, then one LDS fragment read, for every read of the
     // next quarter, then the remaining MFMAs (the reads issue in the shadow of
-    // the MFMAs).
-    auto interleave = [&]() {
+    // the MFMAs); NV loads (at most one per MFMA) are spread evenly over the
+    // quarter's MFMAs.
+    auto interleave = [&](auto nv_c) {
+        constexpr int NV = decltype(nv_c)::value;
+        constexpr int NM = 4 * NTB;
+        static_assert(NV <= NM, "one load per MFMA at most");
 #pragma unroll
-        for (int i = 0; i < 4 + NTB; ++i) {
+        for (int i = 0; i < NM; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i < 4 + NTB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (((i + 1) * NV) / NM > (i * NV) / NM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NTB - (4 + NTB), 0);
     };
-    // After the barrier: the last quarter's MFMAs, the loads of the next
-    // stage and the reads of the next stage's first quarter, one of each in
-    // turn, so no wave stalls on a burst of loads with its MFMAs waiting.
-    auto interleave_loads = [&]() {
+    // After the barrier: the last quarter's MFMAs, NV loads and the reads of
+    // the next stage's first quarter, one of each in turn, so no wave stalls
+    // on a burst of loads with its MFMAs waiting.
+    auto interleave_loads = [&](auto nv_c) {
+        constexpr int NV = decltype(nv_c)::value;
         constexpr int NM = 4 * NTB, NR = 4 + NTB;
-        constexpr int NI = NM > NLD ? NM : NLD;
+        constexpr int NI = NM > NV ? NM : NV;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i < NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     };
-    // Stage kt lives in slot kt % NSLOT and is multiplied in four 16-wide
-    // quarters; the LDS reads of each quarter overlap the MFMAs of the quarter
-    // before.  After the third quarter's MFMAs: wait until this wave's reads
-    // of slot kt % NSLOT are done and its loads of stage kt + 1 have landed
-    // (the loads of later stages may still be in flight); a barrier then makes
-    // stage kt + 1 visible to every wave and tells every wave that slot
-    // kt % NSLOT is free, and the loads of stage kt + NSLOT go there, spread
-    // over the last quarter's MFMAs together with the reads of the first
-    // quarter of stage kt + 1.  Every step issues the same loads and reads
-    // (clamped to the last stage at the end, into slots no later step reads),
-    // so the counts of loads in flight are the same on every path.
+    // Stage kt is multiplied in four 16-wide quarters; the LDS reads of each
+    // quarter overlap the MFMAs of the quarter before.  After the third
+    // quarter's MFMAs: wait until this wave's reads of stage kt are done and
+    // its loads of stage kt + 1 have landed (later loads may still be in
+    // flight); a barrier then makes stage kt + 1 visible to every wave and
+    // tells every wave that stage kt's slots are free.  The reads of the first
+    // quarter of stage kt + 1 and the new loads are spread over the last
+    // quarter's MFMAs.
+    //   NSLOT 2, 3: stage kt is in slot kt % NSLOT; stage kt + NSLOT is
+    //     loaded into it right after the barrier.
+    //   NSLOT 5: A(kt) is in unit 2 kt % 5, B(kt) in unit (2 kt + 1) % 5.
+    //     After the barrier of stage kt, B(kt + 2) is loaded into A(kt)'s unit;
+    //     A(kt + 3) goes into B(kt)'s unit during the first three quarters of
+    //     stage kt + 1, so the loads of a stage never come in one burst, and
+    //     when stage kt ends only A(kt + 2) may still be in flight.
+    // Every step issues the same loads and reads (clamped to the last stage
+    // at the end, into slots no later step reads), so the counts of loads in
+    // flight are the same on every path.
     Frags fa, fb;
+    using IC0 = std::integral_constant<int, 0>;
     auto step = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB) {
         read(cA, cB, 1, fb);
         mma(fa);
-        interleave();
+        interleave(IC0{});
         __builtin_amdgcn_sched_barrier(0);
         read(cA, cB, 2, fa);
         mma(fb);
-        interleave();
+        interleave(IC0{});
         __builtin_amdgcn_sched_barrier(0);
         read(cA, cB, 3, fb);
         mma(fa);
-        interleave();
+        interleave(IC0{});
         __builtin_amdgcn_sched_barrier(0);
         PF_WAIT_LGKM0();
         PF_WAIT_VM(NLD * (NSLOT - 2));
@@ -270,31 +297,149 @@ void ffn_prefill_kernel(
         issue(kt + NSLOT, cA, cB);
         read(nA, nB, 0, fa);
         mma(fb);
-        interleave_loads();
+        interleave_loads(std::integral_constant<int, NLD>{});
         __builtin_amdgcn_sched_barrier(0);
     };
-    issue(0, sA0, sB0);
-    issue(1, sA1, sB1);
-    if (NSLOT > 2) issue(2, sA2, sB2);
-    PF_WAIT_VM(NLD * (NSLOT - 1));
-    __builtin_amdgcn_s_barrier();
-    read(sA0, sB0, 0, fa);
-    const int nk_main = nk - nk % NSLOT;
-    if (NSLOT == 2) {
+    // pA: the unit that receives A(kt + 2) during this step.
+    auto step5 = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB, bf16* pA) {
+        constexpr int V0 = (NJA + 2) / 3, V1 = (NJA + 1) / 3, V2 = NJA / 3;
+        static_assert(V0 + V1 + V2 == NJA, "A loads per quarter");
+        const size_t ko = (size_t)min(kt + 2, nk - 1) * PF_BK;
+        auto ld = [&](int j) {
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[j] + ko),
+                                             (__attribute__((address_space(3))) void*)(pA + 8 * (wave + 4 * j) * PF_BK),
+                                             16, 0, 0);
+        };
+        read(cA, cB, 1, fb);
+#pragma unroll
+        for (int j = 0; j < V0; ++j) ld(j);
+        mma(fa);
+        interleave(std::integral_constant<int, V0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        read(cA, cB, 2, fa);
+#pragma unroll
+        for (int j = V0; j < V0 + V1; ++j) ld(j);
+        mma(fb);
+        interleave(std::integral_constant<int, V1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        read(cA, cB, 3, fb);
+#pragma unroll
+        for (int j = V0 + V1; j < NJA; ++j) ld(j);
+        mma(fa);
+        interleave(std::integral_constant<int, V2>{});
+        __builtin_amdgcn_sched_barrier(0);
+        PF_WAIT_LGKM0();
+        PF_WAIT_VM(NJA);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(kt + 2, cA);
+        read(nA, nB, 0, fa);
+        mma(fb);
+        interleave_loads(std::integral_constant<int, NJB>{});
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // NSLOT 3: stage kt + 2 goes into slot (kt + 2) % 3, freed when stage
+    // kt - 1 ended, with its loads spread over all four quarters of stage kt
+    // (it is needed when stage kt + 1 ends); when stage kt ends only the
+    // loads issued in its first three quarters may still be in flight.
+    auto step3 = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB, bf16* pA, bf16* pB) {
+        constexpr int V = (NLD + 3) / 4;
+        constexpr int V0 = V, V1 = V, V2 = V, V3 = NLD - 3 * V;
+        static_assert(V3 >= 0, "loads per quarter");
+        const size_t ko = (size_t)min(kt + 2, nk - 1) * PF_BK;
+        auto ld = [&](int i) {
+            if (i < NJA)
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[i] + ko),
+                                                 (__attribute__((address_space(3))) void*)(pA + 8 * (wave + 4 * i) * PF_BK),
+                                                 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b_src[i - NJA] + ko),
+                                                 (__attribute__((address_space(3))) void*)(pB + 8 * (wave + 4 * (i - NJA)) * PF_BK),
+                                                 16, 0, 0);
+        };
+        read(cA, cB, 1, fb);
+#pragma unroll
+        for (int i = 0; i < V0; ++i) ld(i);
+        mma(fa);
+        interleave(std::integral_constant<int, V0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        read(cA, cB, 2, fa);
+#pragma unroll
+        for (int i = V0; i < V0 + V1; ++i) ld(i);
+        mma(fb);
+        interleave(std::integral_constant<int, V1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        read(cA, cB, 3, fb);
+#pragma unroll
+        for (int i = V0 + V1; i < V0 + V1 + V2; ++i) ld(i);
+        mma(fa);
+        interleave(std::integral_constant<int, V2>{});
+        __builtin_amdgcn_sched_barrier(0);
+        PF_WAIT_LGKM0();
+        PF_WAIT_VM(V0 + V1 + V2);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = V0 + V1 + V2; i < NLD; ++i) ld(i);
+        read(nA, nB, 0, fa);
+        mma(fb);
+        interleave_loads(std::integral_constant<int, V3>{});
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (HALF) {
+        bf16* const u0 = sA0;
+        bf16* const u1 = sB0;
+        bf16* const u2 = sA1;
+        bf16* const u3 = sB1;
+        bf16* const u4 = sU4;
+        issue_a(0, u0);
+        issue_b(0, u1);
+        issue_a(1, u2);
+        issue_b(1, u3);
+        PF_WAIT_VM(NLD);
+        __builtin_amdgcn_s_barrier();
+        read(u0, u1, 0, fa);
+        const int nk_main = nk - nk % 5;
+        for (int k0 = 0; k0 < nk_main; k0 += 5) {
+            step5(k0, u0, u1, u2, u3, u4);
+            step5(k0 + 1, u2, u3, u4, u0, u1);
+            step5(k0 + 2, u4, u0, u1, u2, u3);
+            step5(k0 + 3, u1, u2, u3, u4, u0);
+            step5(k0 + 4, u3, u4, u0, u1, u2);
+        }
+        // The last nk % 5 stages start again at unit 0.
+        const int rem = nk - nk_main;
+        if (rem > 0) step5(nk_main, u0, u1, u2, u3, u4);
+        if (rem > 1) step5(nk_main + 1, u2, u3, u4, u0, u1);
+        if (rem > 2) step5(nk_main + 2, u4, u0, u1, u2, u3);
+        if (rem > 3) step5(nk_main + 3, u1, u2, u3, u4, u0);
+    } else if (NSLOT == 3) {
+        issue(0, sA0, sB0);
+        issue(1, sA1, sB1);
+        PF_WAIT_VM(NLD);
+        __builtin_amdgcn_s_barrier();
+        read(sA0, sB0, 0, fa);
+        const int nk_main = nk - nk % 3;
+        for (int k0 = 0; k0 < nk_main; k0 += 3) {
+            step3(k0, sA0, sB0, sA1, sB1, sA2, sB2);
+            step3(k0 + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+            step3(k0 + 2, sA2, sB2, sA0, sB0, sA1, sB1);
+        }
+        // The last nk % 3 stages start again at slot 0.
+        if (nk - nk_main > 0) step3(nk_main, sA0, sB0, sA1, sB1, sA2, sB2);
+        if (nk - nk_main > 1) step3(nk_main + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+    } else {
+        issue(0, sA0, sB0);
+        issue(1, sA1, sB1);
+        PF_WAIT_VM(NLD);
+        __builtin_amdgcn_s_barrier();
+        read(sA0, sB0, 0, fa);
+        const int nk_main = nk - nk % 2;
         for (int k0 = 0; k0 < nk_main; k0 += 2) {
             step(k0, sA0, sB0, sA1, sB1);
             step(k0 + 1, sA1, sB1, sA0, sB0);
         }
         if (nk - nk_main > 0) step(nk_main, sA0, sB0, sA1, sB1);
-    } else {
-        for (int k0 = 0; k0 < nk_main; k0 += 3) {
-            step(k0, sA0, sB0, sA1, sB1);
-            step(k0 + 1, sA1, sB1, sA2, sB2);
-            step(k0 + 2, sA2, sB2, sA0, sB0);
-        }
-        // The last nk % 3 stages start again at slot 0.
-        if (nk - nk_main > 0) step(nk_main, sA0, sB0, sA1, sB1);
-        if (nk - nk_main > 1) step(nk_main + 1, sA1, sB1, sA2, sB2);
     }
     PF_WAIT_VM(0);
     PF_WAIT_LGKM0();
@@ -533,7 +678,7 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
     if (K % PF_BK == 0) {
         if (bm == 256)
             MOE_TIMED_LAUNCH(kid, s,
-                             (ffn_prefill_kernel<GATED, 256, 2><<<grid, PF_THREADS, 0, s>>>(
+                             (ffn_prefill_kernel<GATED, 256, 5><<<grid, PF_THREADS, 0, s>>>(
                                  n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
         else
             MOE_TIMED_LAUNCH(kid, s,
