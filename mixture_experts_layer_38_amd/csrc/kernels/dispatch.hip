@@ -18,6 +18,7 @@
 // scatter run as one workgroup instead (same arithmetic, one launch).
 #include "../device_common.h"
 #include "../launch.h"
+#include "dispatch_small.h"
 
 namespace moe {
 
@@ -134,32 +135,8 @@ __global__ __launch_bounds__(kWave) void dispatch_scatter_kernel(
     for (int j = max(beg, S) + lane; j < end; j += kWave) row_assign[j] = -1;
 }
 
-constexpr int DS_SMALL_MAX = 4096;
-
-// Exclusive scan over the 1024 threads of a block (wave scans, then the wave
-// totals in order).  Returns this thread's exclusive prefix; *total gets the sum.
-__device__ __forceinline__ int block_exscan_1024(int v, int* wave_tot, int* total) {
-    const int lane = lane_id();
-    const int wv = threadIdx.x / kWave;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int u = __shfl_up(incl, o);
-        if (lane >= o) incl += u;
-    }
-    if (lane == kWave - 1) wave_tot[wv] = incl;
-    __syncthreads();
-    int before = 0, all = 0;
-    for (int w = 0; w < 1024 / kWave; ++w) {
-        if (w < wv) before += wave_tot[w];
-        all += wave_tot[w];
-    }
-    *total = all;
-    return before + incl - v;
-}
-
 // count + scan + scatter of at most DS_SMALL_MAX assignments in one block of
-// 1024 threads (thread e owns expert e in the scan).
+// 1024 threads.
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     int n, int E, int nbits, int capacity, const int32_t* __restrict__ ids,
     int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
@@ -167,60 +144,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     __shared__ int hist[1024];
     __shared__ int offs[1024];
     __shared__ int wave_tot[1024 / kWave];
-    const int tid = threadIdx.x;
-    hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += 1024) {
-        const int e = ids[i];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
-    }
-    __syncthreads();
-    const int c = tid < E ? hist[tid] : 0;
-    const int kp = tid < E ? (capacity < 0 ? c : min(c, capacity)) : 0;
-    int S = 0;
-    const int excl = block_exscan_1024(kp, wave_tot, &S);
-    if (tid < E) {
-        counts[tid] = c;
-        kept[tid] = kp;
-        offsets[tid] = excl;
-        offs[tid] = excl;
-    }
-    if (tid == 0) offsets[E] = S;
-    hist[tid] = 0;  // from here on: running rank per expert
-    __syncthreads();
-    if (tid < kWave) {
-        const int lane = tid;
-        const unsigned long long below = (1ull << lane) - 1ull;
-        for (int base = 0; base < n; base += kWave) {
-            const int i = base + lane;
-            const bool in = i < n;
-            const int e = in ? ids[i] : -1;
-            const bool ok = in && (unsigned)e < (unsigned)E;
-            unsigned long long peers = __ballot(ok);
-            for (int b = 0; b < nbits; ++b) {
-                const bool bit = ok && ((e >> b) & 1);
-                const unsigned long long bb = __ballot(bit);
-                peers &= bit ? bb : ~bb;
-            }
-            if (ok) {
-                const int r0 = hist[e];
-                const int rank = r0 + __popcll(peers & below);
-                const int last = 63 - __clzll(peers);
-                if (capacity < 0 || rank < capacity) {
-                    const int row = offs[e] + rank;
-                    assign_row[i] = row;
-                    if ((unsigned)row < (unsigned)n) row_assign[row] = i;
-                } else {
-                    assign_row[i] = -1;
-                }
-                if (lane == last) hist[e] = r0 + __popcll(peers);
-            } else if (in) {
-                assign_row[i] = -1;
-            }
-        }
-    }
-    // Rows past the kept total S carry no assignment (disjoint from the rows above).
-    for (int j = S + tid; j < n; j += 1024) row_assign[j] = -1;
+    dispatch_small_block(n, E, nbits, capacity, ids, counts, kept, offsets, assign_row, row_assign, hist,
+                         offs, wave_tot);
 }
 
 __global__ __launch_bounds__(DS_THREADS) void dispatch_gather_kernel(

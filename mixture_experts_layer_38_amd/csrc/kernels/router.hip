@@ -22,6 +22,7 @@
 
 #include "../device_common.h"
 #include "../launch.h"
+#include "dispatch_small.h"
 
 namespace moe {
 
@@ -310,6 +311,158 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(int T, int d, in
     float s = 0.0f;
     for (int j = 0; j < d; ++j) s = fmaf(xr[j], wr[(size_t)j * E + e], s);
     logits[i] = s;
+}
+
+// ---- small batches: two launches for the whole front of the layer -----------
+// For decode-sized batches (T <= 64 tokens, E <= 16 experts):
+//   small_gemm : RS_SLICES workgroups, one slice of d each; the workgroup
+//                copies its rows of W_r (one contiguous block of [d, E]) into
+//                LDS, its four waves take a quarter of the slice each and run
+//                16x16x32 MFMAs of the token rows (read straight from HBM)
+//                against W_r^T fragments gathered from LDS, and the four
+//                quarters are added in order into the slice's partial scores;
+//   route_dispatch_small : one workgroup of 1024 threads adds the slices in
+//                slice order, routes one token per wave (route_token above)
+//                and dispatches the T*K assignments (dispatch_small_block).
+// Same arithmetic as the general kernels except the slicing of d, which only
+// changes fp32 rounding.
+constexpr int RS_SLICES = 16;
+constexpr int RS_MAXT = 64;
+constexpr int RS_MAXE = 16;
+constexpr int RS_WLDS = 8192;  // W_r elements staged per workgroup
+
+__host__ __device__ static inline int rs_kslice(int d) { return ((d + RS_SLICES - 1) / RS_SLICES + 127) / 128 * 128; }
+
+bool route_dispatch_small_ok(int T, int d, int E, int K, int dtype) {
+    return dtype == MOE_DTYPE_BF16 && T >= 1 && T <= RS_MAXT && E <= RS_MAXE && K <= E && d % 8 == 0 &&
+           rs_kslice(d) * E <= RS_WLDS;
+}
+
+size_t route_dispatch_small_ws_bytes(int T, int E) { return align_up((size_t)RS_SLICES * T * E * sizeof(float), 256); }
+
+template <int NTB>
+__global__ __launch_bounds__(256) void small_gemm_kernel(int T, int d, int E, const bf16* __restrict__ x,
+                                                         const bf16* __restrict__ wr, float* __restrict__ part) {
+    __shared__ __align__(16) bf16 wflat[RS_WLDS];
+    __shared__ float red[4][RS_MAXT * RS_MAXE];
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int lane = lane_id();
+    const int rl = lane & 15;
+    const int g = lane >> 4;
+    const int ks = rs_kslice(d);
+    const int kb = blockIdx.x * ks;
+    // rows [kb, kb + ks) of W_r are bytes [2 E kb, 2 E (kb + ks)) of it
+    {
+        const char* src = reinterpret_cast<const char*>(wr) + (size_t)kb * E * 2;
+        const long valid = max(0L, ((long)d - kb) * E * 2);
+        char* dst = reinterpret_cast<char*>(wflat);
+        for (int off = threadIdx.x * 16; off < ks * E * 2; off += 256 * 16)
+            store16(dst + off, load16_or_zero(src + off, off < valid));
+    }
+    // this wave: k in [kb + wave * ks / 4, + ks / 4), in steps of 32
+    const int q = ks / 4;
+    const int kq = kb + wave * q;
+    u32x4 xf[NTB][4];
+    f32x4 acc[NTB];
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < q / 32; s0 += 4) {
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = kq + (s0 + j) * 32 + g * 8;
+                const int t = min(tb * 16 + rl, T - 1);
+                xf[tb][j] = load16_or_zero(x + (size_t)t * d + k, s0 + j < q / 32 && k < d);
+            }
+        if (s0 == 0) __syncthreads();  // W_r rows staged
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (s0 + j < q / 32) {
+                const int kl = wave * q + (s0 + j) * 32 + g * 8;  // local k of the fragment
+                const bf16* wl = wflat + kl * E + min(rl, E - 1);
+                bf16x8 wv;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wv[i] = wl[i * E];
+                if (rl >= E) wv = bf16x8{};
+#pragma unroll
+                for (int tb = 0; tb < NTB; ++tb) acc[tb] = mfma16(as_bf16x8(xf[tb][j]), wv, acc[tb]);
+            }
+        }
+    }
+    // acc[tb][i]: token tb*16 + 4g + i, expert rl
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = tb * 16 + g * 4 + i;
+            if (t < T && rl < E) red[wave][t * E + rl] = acc[tb][i];
+        }
+    __syncthreads();
+    for (int i = threadIdx.x; i < T * E; i += 256)
+        part[(size_t)blockIdx.x * T * E + i] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+}
+
+__global__ __launch_bounds__(1024) void route_dispatch_small_kernel(
+    int T, int E, int K, int flags, int capacity, int nbits, const float* __restrict__ part,
+    const float* __restrict__ bias, float* __restrict__ logits, float* __restrict__ probs,
+    float* __restrict__ prob_sum, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ assign_row, int32_t* __restrict__ row_assign) {
+    __shared__ float lgs[RS_MAXT * RS_MAXE];
+    __shared__ float pw[16][RS_MAXE];
+    __shared__ int sids[RS_MAXT * RS_MAXE];
+    __shared__ int hist[1024];
+    __shared__ int offs[1024];
+    __shared__ int wave_tot[16];
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int lane = lane_id();
+    for (int i = threadIdx.x; i < T * E; i += 1024) {
+        float v = part[i];
+        for (int sl = 1; sl < RS_SLICES; ++sl) v += part[(size_t)sl * T * E + i];
+        lgs[i] = v;
+        if (logits) logits[i] = v;
+    }
+    __syncthreads();
+    float psum[1] = {0.0f};
+    for (int t = wave; t < T; t += 16) {
+        float lg[1] = {lane < E ? lgs[t * E + lane] : 0.0f};
+        route_token<1>(lg, E, K, bias, flags, probs ? probs + (size_t)t * E : nullptr, sids + t * K,
+                       w + (size_t)t * K, psum);
+    }
+    if (lane < E) pw[wave][lane] = psum[0];
+    __syncthreads();
+    if (prob_sum && threadIdx.x < E) {
+        double v = 0.0;
+        for (int sl = 0; sl < 16; ++sl) v += (double)pw[sl][threadIdx.x];
+        prob_sum[threadIdx.x] = (float)v;
+    }
+    for (int i = threadIdx.x; i < T * K; i += 1024) ids[i] = sids[i];
+    dispatch_small_block(T * K, E, nbits, capacity, sids, counts, kept, offsets, assign_row, row_assign,
+                         hist, offs, wave_tot);
+}
+
+hipError_t launch_route_dispatch_small(int T, int d, int E, int K, int flags, int capacity, const void* x,
+                                       const void* w_router, const float* bias, float* logits,
+                                       float* probs, float* prob_sum, int32_t* ids, float* w,
+                                       int32_t* counts, int32_t* kept, int32_t* offsets,
+                                       int32_t* assign_row, int32_t* row_assign, void* ws, hipStream_t s) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    float* part = reinterpret_cast<float*>(ws);
+    const int ntb = (T + 15) / 16;
+    switch (ntb) {
+        case 1: small_gemm_kernel<1><<<RS_SLICES, 256, 0, s>>>(T, d, E, (const bf16*)x, (const bf16*)w_router, part); break;
+        case 2: small_gemm_kernel<2><<<RS_SLICES, 256, 0, s>>>(T, d, E, (const bf16*)x, (const bf16*)w_router, part); break;
+        default: small_gemm_kernel<4><<<RS_SLICES, 256, 0, s>>>(T, d, E, (const bf16*)x, (const bf16*)w_router, part); break;
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER, s,
+                     route_dispatch_small_kernel<<<1, 1024, 0, s>>>(T, E, K, flags, capacity, nbits, part, bias,
+                                                                    logits, probs, prob_sum, ids, w, counts,
+                                                                    kept, offsets, assign_row, row_assign));
+    return hipGetLastError();
 }
 
 // ---- host side ------------------------------------------------------------------

@@ -34,6 +34,16 @@ hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const
                          const void* w_router, const float* bias, float* logits, float* probs,
                          float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s);
 
+// Small batches (bf16, T <= 64, E <= 16): scores, routing and dispatch in two
+// launches, with the outputs of launch_router followed by launch_dispatch
+// (x == NULL there).  ws: route_dispatch_small_ws_bytes.
+bool route_dispatch_small_ok(int T, int d, int E, int K, int dtype);
+size_t route_dispatch_small_ws_bytes(int T, int E);
+hipError_t launch_route_dispatch_small(int T, int d, int E, int K, int flags, int capacity, const void* x,
+                                       const void* w_router, const float* bias, float* logits,
+                                       float* probs, float* prob_sum, int32_t* ids, float* w,
+                                       int32_t* counts, int32_t* kept, int32_t* offsets,
+                                       int32_t* assign_row, int32_t* row_assign, void* ws, hipStream_t s);
 // ---- dispatch --------------------------------------------------------------
 size_t dispatch_ws_bytes(int T, int K, int E);
 hipError_t launch_dispatch(int T, int K, int E, int d, int dtype, int capacity,

@@ -1,5 +1,6 @@
 // C ABI of the MoE layer (include/moe.h): argument checks, workspace layout,
 // and the order of launches.  Never allocates, never synchronises.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -90,7 +91,8 @@ static ForwardLayout forward_layout(const moe_problem* p) {
     L.row_assign = take(n * 4);
     L.act = take(n * F * es);
     L.h = take(n * d * es);
-    L.route_ws = take(router_ws_bytes(p->T, p->d_model, p->n_experts, p->dtype));
+    L.route_ws = take(std::max(router_ws_bytes(p->T, p->d_model, p->n_experts, p->dtype),
+                               route_dispatch_small_ws_bytes(p->T, p->n_experts)));
     L.disp_ws = take(dispatch_ws_bytes(p->T, p->top_k, p->n_experts));
     L.ffn_ws = take(ffn_ws_bytes(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype));
     L.total = o;
@@ -143,16 +145,25 @@ static moe_status forward_launch(const moe_problem* p, const ForwardLayout& L, c
     int32_t* row_assign = D.row_assign ? D.row_assign : (int32_t*)(base + L.row_assign);
     void* act = base + L.act;
     void* h = base + L.h;
-    hipError_t err = launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype,
-                                   (int)p->flags, x, w_router, logit_bias, logits, D.probs,
-                                   D.prob_sum, ids, w, base + L.route_ws, s);
-    if (err != hipSuccess) return MOE_ERR_HIP;
-    // The grouped token rows are never materialised: the first GEMM reads
-    // token row_assign[r] / K for its grouped row r.
-    err = launch_dispatch(p->T, p->top_k, p->n_experts, p->d_model, p->dtype, p->capacity, ids,
-                          nullptr, counts, kept, offsets, assign_row, row_assign, nullptr,
-                          base + L.disp_ws, s);
-    if (err != hipSuccess) return MOE_ERR_HIP;
+    hipError_t err;
+    if (route_dispatch_small_ok(p->T, p->d_model, p->n_experts, p->top_k, p->dtype)) {
+        err = launch_route_dispatch_small(p->T, p->d_model, p->n_experts, p->top_k, (int)p->flags,
+                                          p->capacity, x, w_router, logit_bias, logits, D.probs,
+                                          D.prob_sum, ids, w, counts, kept, offsets, assign_row,
+                                          row_assign, base + L.route_ws, s);
+        if (err != hipSuccess) return MOE_ERR_HIP;
+    } else {
+        err = launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype, (int)p->flags, x,
+                            w_router, logit_bias, logits, D.probs, D.prob_sum, ids, w,
+                            base + L.route_ws, s);
+        if (err != hipSuccess) return MOE_ERR_HIP;
+        // The grouped token rows are never materialised: the first GEMM reads
+        // token row_assign[r] / K for its grouped row r.
+        err = launch_dispatch(p->T, p->top_k, p->n_experts, p->d_model, p->dtype, p->capacity, ids,
+                              nullptr, counts, kept, offsets, assign_row, row_assign, nullptr,
+                              base + L.disp_ws, s);
+        if (err != hipSuccess) return MOE_ERR_HIP;
+    }
     err = launch_ffn(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype, x, row_assign,
                      offsets, w1, w3, w2, act, h, base + L.ffn_ws, s);
     if (err != hipSuccess) return MOE_ERR_HIP;

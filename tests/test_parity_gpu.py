@@ -31,6 +31,9 @@ REDUCED = {
     "k_equals_e": scaled(C["mixtral_decode"], T=40, d=128, E=4, K=4, F=256),
     "top1_decode": scaled(C["mixtral_decode"], T=48, d=512, K=1, F=768),
     "top1_prefill": scaled(C["mixtral_prefill"], T=900, d=320, K=1, F=384),
+    # decode-sized batches that take the one-launch router + dispatch path
+    "small_e16_ragged_d": scaled(C["dsv3_routed"], T=37, d=584, E=16, K=4, F=256),
+    "small_t64_e16": scaled(C["capacity_top2"], T=64, d=256, E=16, F=128),
 }
 
 
@@ -118,14 +121,26 @@ def _check_aux_and_bias(orc, cfg, out, probs):
         f"bias +{int((beta_ref > 0).sum())} -{int((beta_ref < 0).sum())}")
 
 
-def test_aux_and_bias_reduced(orc):
-    cfg = REDUCED["capacity_t2048"]
+@pytest.mark.parametrize("name", ["capacity_t2048", "small_t64_e16"])
+def test_aux_and_bias_reduced(orc, name):
+    cfg = REDUCED[name]
     inp, out, ids, w, probs = _case(orc, cfg)
     _check_aux_and_bias(orc, cfg, out, probs)
 
 
+def test_small_batch_capacity(orc):
+    """A per-expert cap on a decode-sized batch (the one-launch router path)."""
+    base = scaled(C["capacity_top2"], T=48, d=128, E=16, F=128)
+    for cf in (0.0, 0.25, 1.0):
+        cfg = scaled(base, capacity_factor=cf)
+        inp, out, *_ = _case(orc, cfg)
+        if cfg.capacity == 0:
+            assert out["offsets"][-1] == 0 and np.all(out["y"] == 0)
+
+
 @pytest.mark.parametrize("name,flags", [("dsv3_t256", 1), ("capacity_t2048", 2), ("prefill_t600_ragged", 3),
-                                        ("tiny_fp32", 1), ("decode_d512", 2)])
+                                        ("tiny_fp32", 1), ("decode_d512", 2), ("decode_d512", 1),
+                                        ("small_e16_ragged_d", 3)])
 def test_forward_routing_variants(orc, name, flags):
     """Bias for selection only (flag 1), unweighted mean combine (flag 2), both."""
     _case(orc, REDUCED[name], flags=flags)
