@@ -15,7 +15,7 @@ hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* A, con
 hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, const int32_t* rowmap,
                               int topk, const int32_t* offsets, const void* w1, const void* w3,
                               const void* w2, void* act, void* h, void* ws, hipStream_t s);
-size_t prefill_ws_bytes(int n_rows, int E);
+size_t prefill_ws_bytes(int n_rows, int E, int d);
 
 constexpr int kDecodeMaxTokens = 64;
 
@@ -74,9 +74,9 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(int n_rows, int E, in
 
 static bool use_decode(int T, int dtype) { return dtype == MOE_DTYPE_BF16 && T <= kDecodeMaxTokens; }
 
-size_t ffn_ws_bytes(int T, int K, int E, int /*d*/, int /*F*/, int dtype) {
+size_t ffn_ws_bytes(int T, int K, int E, int d, int /*F*/, int dtype) {
     if (dtype != MOE_DTYPE_BF16 || use_decode(T, dtype)) return 256;
-    return prefill_ws_bytes(T * K, E);
+    return prefill_ws_bytes(T * K, E, d);
 }
 
 hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* A,

@@ -30,6 +30,7 @@
 // expert in groups of PF_GM row tiles (row tile fastest inside a group), and
 // XCD x takes the x-th contiguous eighth of that list, so the tiles that run
 // together on one XCD share their token rows and weight rows in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "../device_common.h"
@@ -89,16 +90,61 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int b
     if (e == E - 1) *mt_count = min(start + nt, max_mt);
 }
 
+// Tile t of the grouped order: row tile mt (of expert e, rows [row0, row_end))
+// and weight tile nt.
+struct PfTile {
+    int mt, nt, e, row0, row_end;
+};
+__device__ __forceinline__ PfTile pf_tile(int t, int n_mt, int n_nt, const int32_t* mt_expert,
+                                          const int32_t* mt_row0, const int32_t* offsets, int n_rows) {
+    PfTile r;
+    const int grp = t / (PF_GM * n_nt);
+    const int first = grp * PF_GM;
+    const int gsize = min(PF_GM, n_mt - first);
+    const int rem = t - grp * PF_GM * n_nt;
+    r.mt = first + rem % gsize;
+    r.nt = rem / gsize;
+    r.e = mt_expert[r.mt];
+    r.row0 = mt_row0[r.mt];
+    r.row_end = min(offsets[r.e + 1], n_rows);
+    return r;
+}
+
+// Split of the last, partly filled round of tiles.  Each XCD runs its
+// per_xcd tiles on cpx compute units in rounds of cpx; when the last round
+// holds at most half of cpx tiles, each of those rem tiles is cut into nsplit
+// ranges of k (nsplit * rem <= cpx), whose fp32 partial sums a second kernel
+// adds in range order.  nsplit = 1: no split.
+struct PfSplit {
+    int full, rem, nsplit;
+};
+__host__ __device__ __forceinline__ PfSplit pf_split(int per_xcd, int cpx) {
+    PfSplit r{per_xcd, 0, 1};
+    if (cpx <= 1) return r;
+    const int full = per_xcd / cpx * cpx;
+    const int rem = per_xcd - full;
+    if (rem > 0 && 2 * rem <= cpx) {
+        r.full = full;
+        r.rem = rem;
+        r.nsplit = min(4, cpx / rem);
+    }
+    return r;
+}
+constexpr int PF_MAX_CPX = 32;  // compute units per XCD the split buffer is sized for
+
 // N: weight rows of one expert (gate/up: F, down: d); K: reduction length,
 // a multiple of PF_BK; n_nt: weight tiles per row tile.  BM: token rows per
 // tile (256, or 128 for small expert groups); NSLOT: LDS stages in the ring.
-template <bool GATED, int BM, int NSLOT>
+// SPLIT = false: every tile except the k-split ones of the last round;
+// SPLIT = true: only the k ranges of those (fp32 partial tiles into part).
+template <bool GATED, int BM, int NSLOT, bool SPLIT>
 __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ffn_prefill_kernel(
     int n_rows, int N, int K, int n_nt, const bf16* __restrict__ A,
     const int32_t* __restrict__ rowmap, int topk, const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
     const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ offsets,
-    const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
+    const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out, int cpx,
+    float* __restrict__ part) {
     constexpr int SA = BM * PF_BK;      // bf16 elements of one A stage
     constexpr int SB = PF_BN * PF_BK;   // bf16 elements of one B stage
     constexpr int NTB = BM / 64;        // 32-row token blocks per wave
@@ -116,19 +162,32 @@ void ffn_prefill_kernel(
     const int n_mt = *mt_count;
     const int tiles = n_mt * n_nt;
     const int per_xcd = (tiles + PF_XCD - 1) / PF_XCD;
-    const int slot = blockIdx.x / PF_XCD;
+    const int xcd = blockIdx.x % PF_XCD;
+    int slot = blockIdx.x / PF_XCD;
+    // The gate/up epilogue is not linear in the sums, so only the second GEMM splits.
+    const PfSplit sp = GATED ? PfSplit{per_xcd, 0, 1} : pf_split(per_xcd, cpx);
+    int kpart = 0;
+    constexpr bool split = SPLIT;
+    if (SPLIT) {
+        const int u = slot;
+        if (sp.nsplit <= 1 || u >= sp.rem * sp.nsplit) return;
+        slot = sp.full + u / sp.nsplit;
+        kpart = u % sp.nsplit;
+    } else if (sp.nsplit > 1 && slot >= sp.full) {
+        return;
+    }
     if (slot >= per_xcd) return;
-    const int t = (blockIdx.x % PF_XCD) * per_xcd + slot;
+    const int t = xcd * per_xcd + slot;
     if (t >= tiles) return;
-    const int grp = t / (PF_GM * n_nt);
-    const int first = grp * PF_GM;
-    const int gsize = min(PF_GM, n_mt - first);
-    const int rem = t - grp * PF_GM * n_nt;
-    const int mt = first + rem % gsize;
-    const int nt = rem / gsize;
-    const int e = mt_expert[mt];
-    const int row0 = mt_row0[mt];
-    const int row_end = min(offsets[e + 1], n_rows);
+    const PfTile tl = pf_tile(t, n_mt, n_nt, mt_expert, mt_row0, offsets, n_rows);
+    const int nt = tl.nt;
+    const int e = tl.e;
+    const int row0 = tl.row0;
+    const int row_end = tl.row_end;
+    // k range of this launch unit: all of K, or range kpart of nsplit
+    const int nk_all = K / PF_BK;
+    const int ks0 = split ? nk_all * kpart / sp.nsplit : 0;
+    const int nk = split ? nk_all * (kpart + 1) / sp.nsplit - ks0 : nk_all;
 
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int lane = lane_id();
@@ -148,7 +207,7 @@ void ffn_prefill_kernel(
     for (int j = 0; j < NJA; ++j) {
         const int tr = 8 * (wave + 4 * j) + lr;
         const int r = src_row(rowmap, topk, min(row0 + tr, row_end - 1));
-        a_src[j] = A + (size_t)r * K + (ls ^ pf_swz(tr)) * 8;
+        a_src[j] = A + (size_t)r * K + (size_t)ks0 * PF_BK + (ls ^ pf_swz(tr)) * 8;
     }
 #pragma unroll
     for (int j = 0; j < NJB; ++j) {
@@ -161,13 +220,12 @@ void ffn_prefill_kernel(
             const int blk = (tr >> 5) & 3;
             const int f = min(nt * 128 + w * 64 + (blk >> 1) * 32 + (tr & 31), N - 1);
             const bf16* W = (blk & 1) ? Wb : Wa;
-            b_src[j] = W + ((size_t)e * N + f) * K + c * 8;
+            b_src[j] = W + ((size_t)e * N + f) * K + (size_t)ks0 * PF_BK + c * 8;
         } else {
             const int nr = min(nt * PF_BN + tr, N - 1);
-            b_src[j] = Wa + ((size_t)e * N + nr) * K + c * 8;
+            b_src[j] = Wa + ((size_t)e * N + nr) * K + (size_t)ks0 * PF_BK + c * 8;
         }
     }
-    const int nk = K / PF_BK;
     auto issue_a = [&](int kt, bf16* dA) {
         const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
@@ -446,6 +504,23 @@ void ffn_prefill_kernel(
 
     // acc[wb][tb][i]: weight row 8*(i/4) + 4*(lane/32) + i%4 of block wb,
     // token lane % 32 of block tb.
+    if (SPLIT) {
+        // fp32 partial tile [BM][PF_BN], row = token, column = weight row
+        float* pt = part + (size_t)((xcd * sp.rem + (slot - sp.full)) * sp.nsplit + kpart) * BM * PF_BN;
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            float* prow = pt + (size_t)(wm * (BM / 2) + tb * 32 + (lane & 31)) * PF_BN;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int wb = 0; wb < 4; ++wb) {
+                    const f32x16& a = acc[wb][tb];
+                    *reinterpret_cast<f32x4*>(prow + wn * 128 + wb * 32 + 8 * q + 4 * (lane >> 5)) =
+                        f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
         const int grow = row0 + wm * (BM / 2) + tb * 32 + (lane & 31);
@@ -661,8 +736,67 @@ __global__ __launch_bounds__(PG_THREADS) void ffn_prefill_generic_kernel(
     }
 }
 
-size_t prefill_ws_bytes(int n_rows, int E) {
+// Adds the nsplit partial tiles of each split tile in range order and writes
+// the bf16 rows of the second GEMM.  One workgroup per possible split tile
+// (XCD b % 8, tile b / 8 of the XCD's last round).
+template <int BM>
+__global__ __launch_bounds__(256) void ffn_split_reduce_kernel(
+    int n_rows, int N, int n_nt, int cpx, const int32_t* __restrict__ mt_count,
+    const int32_t* __restrict__ mt_expert, const int32_t* __restrict__ mt_row0,
+    const int32_t* __restrict__ offsets, const float* __restrict__ part, bf16* __restrict__ out) {
+    const int n_mt = *mt_count;
+    const int tiles = n_mt * n_nt;
+    const int per_xcd = (tiles + PF_XCD - 1) / PF_XCD;
+    const PfSplit sp = pf_split(per_xcd, cpx);
+    const int xcd = blockIdx.x % PF_XCD;
+    const int r = blockIdx.x / PF_XCD;
+    if (sp.nsplit <= 1 || r >= sp.rem) return;
+    const int t = xcd * per_xcd + sp.full + r;
+    if (t >= tiles) return;
+    const PfTile tl = pf_tile(t, n_mt, n_nt, mt_expert, mt_row0, offsets, n_rows);
+    const size_t tsz = (size_t)BM * PF_BN;
+    const float* p0 = part + (size_t)((xcd * sp.rem + r) * sp.nsplit) * tsz;
+    for (int i = threadIdx.x * 4; i < BM * PF_BN; i += 256 * 4) {
+        const int row = i / PF_BN;
+        const int col = i % PF_BN;
+        const int grow = tl.row0 + row;
+        const int gcol = tl.nt * PF_BN + col;
+        if (grow >= tl.row_end || gcol >= N) continue;
+        f32x4 v = *reinterpret_cast<const f32x4*>(p0 + i);
+        for (int p = 1; p < sp.nsplit; ++p) v += *reinterpret_cast<const f32x4*>(p0 + (size_t)p * tsz + i);
+        bf16* o = out + (size_t)grow * N + gcol;
+        if (gcol + 3 < N) {
+            *reinterpret_cast<bf16x4*>(o) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        } else {
+            for (int q = 0; q < 4; ++q)
+                if (gcol + q < N) o[q] = (bf16)v[q];
+        }
+    }
+}
+
+// Compute units per XCD (0: no split), from the current device.
+static int prefill_cpx() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (cus % PF_XCD != 0) return 0;
+    return min(cus / PF_XCD, PF_MAX_CPX);
+}
+
+// Partial tiles of the split: at most PF_MAX_CPX per XCD, and at most four
+// per tile of the second GEMM.
+static size_t prefill_split_bytes(int n_rows, int E, int d) {
+    const size_t parts = std::min((size_t)PF_XCD * PF_MAX_CPX,
+                                  (size_t)4 * prefill_max_mtiles(n_rows, E) * ((d + PF_BN - 1) / PF_BN));
+    return align_up(parts * PF_BM_MAX * PF_BN * sizeof(float), 256);
+}
+
+static size_t prefill_plan_bytes(int n_rows, int E) {
     return align_up((size_t)(1 + 2 * prefill_max_mtiles(n_rows, E)) * sizeof(int32_t), 256);
+}
+
+size_t prefill_ws_bytes(int n_rows, int E, int d) {
+    return prefill_plan_bytes(n_rows, E) + prefill_split_bytes(n_rows, E, d);
 }
 
 template <bool GATED>
@@ -671,21 +805,43 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
                                       const int32_t* mt_count,
                                       const int32_t* mt_expert, const int32_t* mt_row0,
                                       const int32_t* offsets, const bf16* Wa, const bf16* Wb,
-                                      bf16* out, hipStream_t s) {
+                                      bf16* out, float* part, hipStream_t s) {
     const long tiles = (long)max_mt * n_nt;
-    const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
     const int kid = GATED ? MOE_KERNEL_FFN_GATE_UP : MOE_KERNEL_FFN_DOWN;
     if (K % PF_BK == 0) {
+        // the second GEMM may cut its last round into k ranges (K >= 4 stages)
+        const int cpx = (!GATED && K / PF_BK >= 4) ? prefill_cpx() : 0;
+        const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
+        const unsigned sgrid = (unsigned)(PF_XCD * cpx);  // split units: at most cpx per XCD
         if (bm == 256)
             MOE_TIMED_LAUNCH(kid, s,
-                             (ffn_prefill_kernel<GATED, 256, 5><<<grid, PF_THREADS, 0, s>>>(
-                                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
+                             (ffn_prefill_kernel<GATED, 256, 5, false><<<grid, PF_THREADS, 0, s>>>(
+                                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out,
+                                 cpx, part)));
         else
             MOE_TIMED_LAUNCH(kid, s,
-                             (ffn_prefill_kernel<GATED, 128, 3><<<grid, PF_THREADS, 0, s>>>(
-                                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out)));
+                             (ffn_prefill_kernel<GATED, 128, 3, false><<<grid, PF_THREADS, 0, s>>>(
+                                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out,
+                                 cpx, part)));
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess || cpx == 0 || GATED) return err;
+        if (bm == 256)
+            ffn_prefill_kernel<false, 256, 5, true><<<sgrid, PF_THREADS, 0, s>>>(
+                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
+        else
+            ffn_prefill_kernel<false, 128, 3, true><<<sgrid, PF_THREADS, 0, s>>>(
+                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        const unsigned rgrid = (unsigned)(PF_XCD * (cpx / 2));
+        if (bm == 256)
+            ffn_split_reduce_kernel<256><<<rgrid, 256, 0, s>>>(n_rows, N, n_nt, cpx, mt_count, mt_expert, mt_row0,
+                                                               offsets, part, out);
+        else
+            ffn_split_reduce_kernel<128><<<rgrid, 256, 0, s>>>(n_rows, N, n_nt, cpx, mt_count, mt_expert, mt_row0,
+                                                               offsets, part, out);
         return hipGetLastError();
     }
+    const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void*)ffn_prefill_generic_kernel<GATED>,
@@ -716,17 +872,18 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
     int32_t* mt_count = reinterpret_cast<int32_t*>(ws);
     int32_t* mt_expert = mt_count + 1;
     int32_t* mt_row0 = mt_expert + max_mt;
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + prefill_plan_bytes(n_rows, E));
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_PLAN, s,
                      ffn_plan_kernel<<<1, 1024, 0, s>>>(E, max_mt, bm, offsets, mt_count, mt_expert, mt_row0));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, (const bf16*)A,
                                     rowmap, topk, mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
-                                    (const bf16*)w3, (bf16*)act, s);
+                                    (const bf16*)w3, (bf16*)act, nullptr, s);
     if (err != hipSuccess) return err;
     return launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
                                       (const bf16*)act, nullptr, 1, mt_count, mt_expert, mt_row0, offsets,
-                                      (const bf16*)w2, nullptr, (bf16*)h, s);
+                                      (const bf16*)w2, nullptr, (bf16*)h, part, s);
 }
 
 }  // namespace moe
