@@ -228,62 +228,97 @@ __global__ __launch_bounds__(256) void router_transpose_kernel(int d, int E, con
 }
 
 // out[split][t][e] = sum over d in this split's slice of x[t][k] * W_r^T[e][k].
-// Wave tile: 16 tokens x 16*NEB experts; lane (r = lane % 16, g = lane / 16).
-// In each 32-wide slice of a 128-wide chunk the four lanes of a row read 64
-// contiguous bytes; both operands use the same k order.
+// Workgroup tile: 64 tokens (16 per wave) x 16*NEB experts.  The W_r^T rows
+// of each 128-wide chunk of d are shared by the four waves through LDS: they
+// arrive by DMA (global_load_lds) into one of two buffers while the other is
+// multiplied, with chunk c of row r in slot c ^ (r % 16) so that the fragment
+// reads of 16 consecutive rows fall in distinct banks.  Token rows come
+// straight from HBM one chunk ahead.  Lane (r = lane % 16, g = lane / 16); in
+// each 32-wide step both operands take k = 32 s + 8 g + [0, 8).
 template <int NEB>
 __global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, int kspan,
                                                          const bf16* __restrict__ x,
                                                          const bf16* __restrict__ wrt,
                                                          float* __restrict__ out) {
+    constexpr int ROWS = 16 * NEB;                // W_r^T rows per workgroup
+    constexpr int CH = ROWS * RG_KCH;             // bf16 elements of one chunk
+    constexpr int NLD = ROWS * RG_KCH * 2 / 16 / 256;  // 16-byte DMA loads per thread per chunk
+    static_assert(NLD >= 1, "chunk covers the workgroup");
+    __shared__ __align__(1024) bf16 wb0[CH], wb1[CH];
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int lane = lane_id();
     const int rl = lane & 15;
     const int g = lane >> 4;
     const int tb = blockIdx.x * 4 + wave;
-    if (tb * 16 >= T) return;  // no barrier in this kernel
-    const int eb0 = blockIdx.y * 16 * NEB;
+    const bool active = tb * 16 < T;  // idle waves still take part in the loads and barriers
+    const int eb0 = blockIdx.y * ROWS;
     const int k_beg = blockIdx.z * kspan;
     const int k_end = min(d, k_beg + kspan);
+    const int nch = max(0, (k_end - k_beg + RG_KCH - 1) / RG_KCH);
+    // DMA: thread p fills LDS slots p + 256 i (16 bytes each) = row (p + 256 i) / 16,
+    // slot (p + 256 i) % 16, holding chunk slot ^ (row % 16) of that row.
+    const bf16* wsrc[NLD];
+    int wcol[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int q = (int)threadIdx.x + 256 * i;
+        const int row = q / 16;
+        wcol[i] = ((q % 16) ^ (row & 15)) * 8;
+        wsrc[i] = wrt + (size_t)min(eb0 + row, E - 1) * d;
+    }
+    auto issue = [&](int c, bf16* dst) {
+        const int kc = k_beg + min(c, max(nch - 1, 0)) * RG_KCH;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(wsrc[i] + min(kc + wcol[i], d - 8)),
+                (__attribute__((address_space(3))) void*)(dst + (size_t)(wave * kWave + 256 * i) * 8), 16, 0, 0);
+    };
     const int kl = g * 8;
     const bf16* xr = x + (size_t)min(tb * 16 + rl, T - 1) * d + kl;
-    const bf16* wrow[NEB];
-#pragma unroll
-    for (int j = 0; j < NEB; ++j) wrow[j] = wrt + (size_t)min(eb0 + j * 16 + rl, E - 1) * d + kl;
     f32x4 acc[NEB];
 #pragma unroll
     for (int j = 0; j < NEB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nch = (k_end - k_beg + RG_KCH - 1) / RG_KCH;
     u32x4 xc[4], xn[4];
+    issue(0, wb0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int k = k_beg + s * 32;
-        xc[s] = load16_or_zero(xr + k, k + kl < k_end);
+        xc[s] = load16_or_zero(xr + k, active && k + kl < k_end);
     }
     for (int c = 0; c < nch; ++c) {
-        const int kc = k_beg + c * RG_KCH;
-        u32x4 wv[NEB][4];
+        bf16* cur = (c & 1) ? wb1 : wb0;
+        bf16* nxt = (c & 1) ? wb0 : wb1;
+        // chunk c has landed and every wave is done with chunk c - 1's buffer
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only: this thread's loads of chunk c
+        __syncthreads();
+        issue(c + 1, nxt);
+        const int kn = k_beg + (c + 1) * RG_KCH;
 #pragma unroll
-        for (int j = 0; j < NEB; ++j)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = kc + s * 32;
-                wv[j][s] = load16_or_zero(wrow[j] + k, k + kl < k_end);
-            }
-        if (c + 1 < nch) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = kc + RG_KCH + s * 32;
-                xn[s] = load16_or_zero(xr + k, k + kl < k_end);
-            }
+        for (int s = 0; s < 4; ++s) {
+            const int k = kn + s * 32;
+            xn[s] = load16_or_zero(xr + k, active && c + 1 < nch && k + kl < k_end);
         }
+        // W_r^T fragments of step s + 1 are read while step s is multiplied
+        bf16x8 wv[2][NEB];
+        auto rd = [&](int s, bf16x8 (&f)[NEB]) {
+            const int slot = ((4 * s + g) ^ rl) * 8;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+            for (int j = 0; j < NEB; ++j)
+                f[j] = *reinterpret_cast<const bf16x8*>(cur + (j * 16 + rl) * RG_KCH + slot);
+        };
+        rd(0, wv[0]);
 #pragma unroll
-            for (int j = 0; j < NEB; ++j) acc[j] = mfma16(as_bf16x8(xc[s]), as_bf16x8(wv[j][s]), acc[j]);
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) rd(s + 1, wv[(s + 1) & 1]);
+#pragma unroll
+            for (int j = 0; j < NEB; ++j) acc[j] = mfma16(as_bf16x8(xc[s]), wv[s & 1][j], acc[j]);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) xc[s] = xn[s];
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may outlive the workgroup
+    if (!active) return;
     // acc[j][i]: token tb*16 + 4g + i, expert eb0 + 16 j + rl
     float* o = out + (size_t)blockIdx.z * T * E;
 #pragma unroll
