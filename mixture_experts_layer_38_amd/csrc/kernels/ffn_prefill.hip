@@ -737,8 +737,11 @@ __global__ __launch_bounds__(PG_THREADS) void ffn_prefill_generic_kernel(
 }
 
 // Adds the nsplit partial tiles of each split tile in range order and writes
-// the bf16 rows of the second GEMM.  One workgroup per possible split tile
-// (XCD b % 8, tile b / 8 of the XCD's last round).
+// the bf16 rows of the second GEMM.  Workgroup (b, y): split tile b / 8 of XCD
+// b % 8, rows [16 y, 16 y + 16) of it; every thread issues all its loads at
+// once (PF_RD_V float4 of each partial tile).
+constexpr int PF_RD_ROWS = 16;
+constexpr int PF_RD_V = PF_RD_ROWS * PF_BN / 4 / 256;
 template <int BM>
 __global__ __launch_bounds__(256) void ffn_split_reduce_kernel(
     int n_rows, int N, int n_nt, int cpx, const int32_t* __restrict__ mt_count,
@@ -754,22 +757,29 @@ __global__ __launch_bounds__(256) void ffn_split_reduce_kernel(
     const int t = xcd * per_xcd + sp.full + r;
     if (t >= tiles) return;
     const PfTile tl = pf_tile(t, n_mt, n_nt, mt_expert, mt_row0, offsets, n_rows);
+    const int rb = blockIdx.y * PF_RD_ROWS;
+    if (tl.row0 + rb >= tl.row_end) return;
     const size_t tsz = (size_t)BM * PF_BN;
-    const float* p0 = part + (size_t)((xcd * sp.rem + r) * sp.nsplit) * tsz;
-    for (int i = threadIdx.x * 4; i < BM * PF_BN; i += 256 * 4) {
-        const int row = i / PF_BN;
-        const int col = i % PF_BN;
-        const int grow = tl.row0 + row;
-        const int gcol = tl.nt * PF_BN + col;
+    const float* p0 = part + (size_t)((xcd * sp.rem + r) * sp.nsplit) * tsz + (size_t)rb * PF_BN;
+    f32x4 v[PF_RD_V];
+#pragma unroll
+    for (int u = 0; u < PF_RD_V; ++u) v[u] = *reinterpret_cast<const f32x4*>(p0 + (u * 256 + threadIdx.x) * 4);
+    for (int p = 1; p < sp.nsplit; ++p)
+#pragma unroll
+        for (int u = 0; u < PF_RD_V; ++u)
+            v[u] += *reinterpret_cast<const f32x4*>(p0 + p * tsz + (u * 256 + threadIdx.x) * 4);
+#pragma unroll
+    for (int u = 0; u < PF_RD_V; ++u) {
+        const int i = (u * 256 + threadIdx.x) * 4;
+        const int grow = tl.row0 + rb + i / PF_BN;
+        const int gcol = tl.nt * PF_BN + i % PF_BN;
         if (grow >= tl.row_end || gcol >= N) continue;
-        f32x4 v = *reinterpret_cast<const f32x4*>(p0 + i);
-        for (int p = 1; p < sp.nsplit; ++p) v += *reinterpret_cast<const f32x4*>(p0 + (size_t)p * tsz + i);
         bf16* o = out + (size_t)grow * N + gcol;
         if (gcol + 3 < N) {
-            *reinterpret_cast<bf16x4*>(o) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+            *reinterpret_cast<bf16x4*>(o) = bf16x4{(bf16)v[u][0], (bf16)v[u][1], (bf16)v[u][2], (bf16)v[u][3]};
         } else {
             for (int q = 0; q < 4; ++q)
-                if (gcol + q < N) o[q] = (bf16)v[q];
+                if (gcol + q < N) o[q] = (bf16)v[u][q];
         }
     }
 }
@@ -832,7 +842,7 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
             ffn_prefill_kernel<false, 128, 3, true><<<sgrid, PF_THREADS, 0, s>>>(
                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        const unsigned rgrid = (unsigned)(PF_XCD * (cpx / 2));
+        const dim3 rgrid((unsigned)(PF_XCD * (cpx / 2)), (unsigned)(bm / PF_RD_ROWS));
         if (bm == 256)
             ffn_split_reduce_kernel<256><<<rgrid, 256, 0, s>>>(n_rows, N, n_nt, cpx, mt_count, mt_expert, mt_row0,
                                                                offsets, part, out);
