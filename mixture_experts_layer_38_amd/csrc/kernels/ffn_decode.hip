@@ -36,16 +36,16 @@ __device__ __forceinline__ u32x4 load16_masked(const bf16* row, int k, int K) {
     return k < K ? v : z;
 }
 
+// The rows of expert e against this workgroup's strip of weight rows.
 template <bool GATED, int CPI, int NCB, bool ALIGNED, int R>
-__global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
-    int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
+__device__ __forceinline__ void ffn_decode_group(
+    int e, int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
     const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
     bf16* __restrict__ out) {
     constexpr int NG = GATED ? 2 : 1;
     constexpr int NS = 4 * CPI;          // 32-wide slices per chunk
     constexpr int KCH = DC_KCH * CPI;  // k per chunk
     __shared__ float red[DC_WAVES - 1][R][NCB][NG][4][kWave];
-    const int e = blockIdx.y;
     const int n0 = blockIdx.x * DC_ROWS * R;
     const int r0 = offsets[e];
     const int m = min(offsets[e + 1], n_rows) - r0;
@@ -189,6 +189,27 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
     }
 }
 
+template <bool GATED, int CPI, int NCB, bool ALIGNED, int R>
+__global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
+    int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
+    const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
+    bf16* __restrict__ out) {
+    ffn_decode_group<GATED, CPI, NCB, ALIGNED, R>(blockIdx.y, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out);
+}
+
+// The experts listed in elist[0 .. *ecount) (small groups of a large batch),
+// taken in turn by the gridDim.y workgroups of each strip.
+template <bool GATED, int CPI, int NCB, bool ALIGNED, int R>
+__global__ __launch_bounds__(DC_WAVES * kWave) void ffn_small_experts_kernel(
+    int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ elist, const int32_t* __restrict__ ecount,
+    const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
+    const int cnt = *ecount;
+    for (int i = blockIdx.y; i < cnt; i += gridDim.y)
+        ffn_decode_group<GATED, CPI, NCB, ALIGNED, R>(elist[i], n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb,
+                                                      out);
+}
+
 template <bool ALIGNED>
 static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A,
                                   const int32_t* rowmap, int topk, const int32_t* offsets,
@@ -208,6 +229,39 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A
                      ffn_decode_kernel<false, 1, 1, ALIGNED, 2><<<g2, DC_WAVES * kWave, 0, s>>>(
                          n_rows, d, F, (const bf16*)act, nullptr, 1, offsets, (const bf16*)w2, nullptr, (bf16*)h));
     return hipGetLastError();
+}
+
+// Experts with at most DC_SMALL_ROWS rows inside a larger batch (listed by the
+// tile plan): one pass of 32 token rows over each weight row, so every weight
+// byte is read once; DC_SMALL_GY workgroups per strip take the experts in turn.
+constexpr int DC_SMALL_GY = 16;
+template <bool ALIGNED>
+static hipError_t launch_small_experts_t(bool gated, int n_rows, int N, int K, const void* A,
+                                         const int32_t* rowmap, int topk, const int32_t* offsets,
+                                         const int32_t* elist, const int32_t* ecount, const void* wa,
+                                         const void* wb, void* out, hipStream_t s) {
+    if (gated) {
+        dim3 g((N + DC_ROWS - 1) / DC_ROWS, DC_SMALL_GY);
+        ffn_small_experts_kernel<true, 1, 2, ALIGNED, 1><<<g, DC_WAVES * kWave, 0, s>>>(
+            n_rows, N, K, (const bf16*)A, rowmap, topk, offsets, elist, ecount, (const bf16*)wa, (const bf16*)wb,
+            (bf16*)out);
+    } else {
+        dim3 g((N + 2 * DC_ROWS - 1) / (2 * DC_ROWS), DC_SMALL_GY);
+        ffn_small_experts_kernel<false, 1, 2, ALIGNED, 2><<<g, DC_WAVES * kWave, 0, s>>>(
+            n_rows, N, K, (const bf16*)A, nullptr, 1, offsets, elist, ecount, (const bf16*)wa, nullptr,
+            (bf16*)out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_small_experts(bool gated, int n_rows, int N, int K, const void* A, const int32_t* rowmap,
+                                int topk, const int32_t* offsets, const int32_t* elist, const int32_t* ecount,
+                                const void* wa, const void* wb, void* out, hipStream_t s) {
+    if (K % DC_KCH == 0)
+        return launch_small_experts_t<true>(gated, n_rows, N, K, A, rowmap, topk, offsets, elist, ecount, wa, wb,
+                                            out, s);
+    return launch_small_experts_t<false>(gated, n_rows, N, K, A, rowmap, topk, offsets, elist, ecount, wa, wb,
+                                         out, s);
 }
 
 hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* A, const int32_t* rowmap,

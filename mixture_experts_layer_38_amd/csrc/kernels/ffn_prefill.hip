@@ -44,6 +44,7 @@ constexpr int PF_THREADS = 256;
 constexpr int PF_BM_MAX = 256;      // token rows per tile: 256, or 128 for small groups
 constexpr int PF_GM = 8;            // row tiles per group in the tile order
 constexpr int PF_XCD = 8;
+constexpr int PF_SMALL_MIN_E = 32;  // experts from which small groups leave the tiled GEMM
 
 // Swizzle of the eight 16-byte chunks of a 128-byte tile row: row r keeps
 // chunk c in slot c ^ pf_swz(r), so fragment reads of consecutive rows (one
@@ -59,16 +60,35 @@ int prefill_max_mtiles(int n_rows, int E) { return n_rows / 128 + E + 1; }
 
 // One block; thread e cuts expert e's rows into bm-row tiles: *mt_count
 // row tiles, tile j of expert mt_expert[j] starting at grouped row mt_row0[j].
-__global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int bm,
+__global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int bm, int min_rows,
                                                        const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ mt_count,
                                                        int32_t* __restrict__ mt_expert,
-                                                       int32_t* __restrict__ mt_row0) {
+                                                       int32_t* __restrict__ mt_row0,
+                                                       int32_t* __restrict__ small_count,
+                                                       int32_t* __restrict__ small_list) {
     __shared__ int wave_tot[1024 / kWave];
+    __shared__ int small_tot[1024 / kWave];
     const int e = threadIdx.x;
     const int lane = e & (kWave - 1);
     const int wv = e / kWave;
-    const int rows = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    const int rows0 = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    // Experts with 1 .. min_rows rows leave the tiled GEMM when they are at
+    // least a quarter of all experts (a skewed routing); otherwise every
+    // expert stays in it.  Listed in expert order.
+    const int sm0 = (e < E && rows0 > 0 && rows0 <= min_rows) ? 1 : 0;
+    const unsigned long long bal = __ballot(sm0);
+    if (lane == 0) small_tot[wv] = __popcll(bal);
+    __syncthreads();
+    int sbefore = 0, sall = 0;
+    for (int w = 0; w < 1024 / kWave; ++w) {
+        if (w < wv) sbefore += small_tot[w];
+        sall += small_tot[w];
+    }
+    const bool split_small = 4 * sall >= E;
+    if (split_small && sm0) small_list[sbefore + __popcll(bal & ((1ull << lane) - 1ull))] = e;
+    if (e == 0) *small_count = split_small ? sall : 0;
+    const int rows = (split_small && sm0) ? 0 : rows0;
     const int nt = (rows + bm - 1) / bm;
     int incl = nt;
 #pragma unroll
@@ -801,8 +821,9 @@ static size_t prefill_split_bytes(int n_rows, int E, int d) {
     return align_up(parts * PF_BM_MAX * PF_BN * sizeof(float), 256);
 }
 
+// Plan: [mt_count][mt_expert][mt_row0][small_count][small_list (E)].
 static size_t prefill_plan_bytes(int n_rows, int E) {
-    return align_up((size_t)(1 + 2 * prefill_max_mtiles(n_rows, E)) * sizeof(int32_t), 256);
+    return align_up((size_t)(2 + 2 * prefill_max_mtiles(n_rows, E) + E) * sizeof(int32_t), 256);
 }
 
 size_t prefill_ws_bytes(int n_rows, int E, int d) {
@@ -882,18 +903,32 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
     int32_t* mt_count = reinterpret_cast<int32_t*>(ws);
     int32_t* mt_expert = mt_count + 1;
     int32_t* mt_row0 = mt_expert + max_mt;
+    int32_t* small_count = mt_row0 + max_mt;
+    int32_t* small_list = small_count + 1;
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + prefill_plan_bytes(n_rows, E));
+    // With many experts some groups are small: those stream their weights
+    // through the decode kernel instead of padding a row tile.
+    const int small = (E >= PF_SMALL_MIN_E) ? DC_SMALL_ROWS : 0;
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_PLAN, s,
-                     ffn_plan_kernel<<<1, 1024, 0, s>>>(E, max_mt, bm, offsets, mt_count, mt_expert, mt_row0));
+                     ffn_plan_kernel<<<1, 1024, 0, s>>>(E, max_mt, bm, small, offsets, mt_count, mt_expert,
+                                                        mt_row0, small_count, small_list));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, (const bf16*)A,
                                     rowmap, topk, mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
                                     (const bf16*)w3, (bf16*)act, nullptr, s);
     if (err != hipSuccess) return err;
-    return launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
-                                      (const bf16*)act, nullptr, 1, mt_count, mt_expert, mt_row0, offsets,
-                                      (const bf16*)w2, nullptr, (bf16*)h, part, s);
+    if (small) {
+        err = launch_small_experts(true, n_rows, F, d, A, rowmap, topk, offsets, small_list, small_count, w1, w3,
+                                   act, s);
+        if (err != hipSuccess) return err;
+    }
+    err = launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
+                                     (const bf16*)act, nullptr, 1, mt_count, mt_expert, mt_row0, offsets,
+                                     (const bf16*)w2, nullptr, (bf16*)h, part, s);
+    if (err != hipSuccess || !small) return err;
+    return launch_small_experts(false, n_rows, d, F, act, nullptr, 1, offsets, small_list, small_count, w2,
+                                nullptr, h, s);
 }
 
 }  // namespace moe
