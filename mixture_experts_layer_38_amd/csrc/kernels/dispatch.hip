@@ -24,8 +24,11 @@ namespace moe {
 
 constexpr int DS_THREADS = 256;
 
+// Chunk of the flat assignment list per count block / scatter wave: small
+// enough that the scatter's serial rounds stay few, large enough that the scan
+// over blocks stays short.
 static int dispatch_chunk(int n) {
-    int ch = 1024;
+    int ch = 256;
     while ((n + ch - 1) / ch > 2048) ch *= 2;
     return ch;
 }
@@ -68,10 +71,16 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int nblk, int E, in
     const int wv = e / kWave;
     int run = 0;
     if (e < E) {
-        for (int b = 0; b < nblk; ++b) {
-            const int c = blk[(size_t)b * E + e];
-            blk[(size_t)b * E + e] = run;  // exclusive base of block b for expert e
-            run += c;
+        // loads issued 16 at a time, then the running sum in block order
+        for (int b0 = 0; b0 < nblk; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) c[q] = b0 + q < nblk ? blk[(size_t)(b0 + q) * E + e] : 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                if (b0 + q < nblk) blk[(size_t)(b0 + q) * E + e] = run;  // exclusive base of block b for expert e
+                run += c[q];
+            }
         }
         counts[e] = run;
     }

@@ -233,20 +233,19 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A
 
 // Experts with at most DC_SMALL_ROWS rows inside a larger batch (listed by the
 // tile plan): one pass of 32 token rows over each weight row, so every weight
-// byte is read once; DC_SMALL_GY workgroups per strip take the experts in turn.
-constexpr int DC_SMALL_GY = 16;
+// byte is read once; gy = min(E, 64) workgroups per strip take the experts in turn.
 template <bool ALIGNED>
-static hipError_t launch_small_experts_t(bool gated, int n_rows, int N, int K, const void* A,
+static hipError_t launch_small_experts_t(bool gated, int gy, int n_rows, int N, int K, const void* A,
                                          const int32_t* rowmap, int topk, const int32_t* offsets,
                                          const int32_t* elist, const int32_t* ecount, const void* wa,
                                          const void* wb, void* out, hipStream_t s) {
     if (gated) {
-        dim3 g((N + DC_ROWS - 1) / DC_ROWS, DC_SMALL_GY);
+        dim3 g((N + DC_ROWS - 1) / DC_ROWS, gy);
         ffn_small_experts_kernel<true, 1, 2, ALIGNED, 1><<<g, DC_WAVES * kWave, 0, s>>>(
             n_rows, N, K, (const bf16*)A, rowmap, topk, offsets, elist, ecount, (const bf16*)wa, (const bf16*)wb,
             (bf16*)out);
     } else {
-        dim3 g((N + 2 * DC_ROWS - 1) / (2 * DC_ROWS), DC_SMALL_GY);
+        dim3 g((N + 2 * DC_ROWS - 1) / (2 * DC_ROWS), gy);
         ffn_small_experts_kernel<false, 1, 2, ALIGNED, 2><<<g, DC_WAVES * kWave, 0, s>>>(
             n_rows, N, K, (const bf16*)A, nullptr, 1, offsets, elist, ecount, (const bf16*)wa, nullptr,
             (bf16*)out);
@@ -254,14 +253,15 @@ static hipError_t launch_small_experts_t(bool gated, int n_rows, int N, int K, c
     return hipGetLastError();
 }
 
-hipError_t launch_small_experts(bool gated, int n_rows, int N, int K, const void* A, const int32_t* rowmap,
-                                int topk, const int32_t* offsets, const int32_t* elist, const int32_t* ecount,
-                                const void* wa, const void* wb, void* out, hipStream_t s) {
+hipError_t launch_small_experts(bool gated, int E, int n_rows, int N, int K, const void* A,
+                                const int32_t* rowmap, int topk, const int32_t* offsets, const int32_t* elist,
+                                const int32_t* ecount, const void* wa, const void* wb, void* out, hipStream_t s) {
+    const int gy = E < 64 ? E : 64;
     if (K % DC_KCH == 0)
-        return launch_small_experts_t<true>(gated, n_rows, N, K, A, rowmap, topk, offsets, elist, ecount, wa, wb,
-                                            out, s);
-    return launch_small_experts_t<false>(gated, n_rows, N, K, A, rowmap, topk, offsets, elist, ecount, wa, wb,
-                                         out, s);
+        return launch_small_experts_t<true>(gated, gy, n_rows, N, K, A, rowmap, topk, offsets, elist, ecount, wa,
+                                            wb, out, s);
+    return launch_small_experts_t<false>(gated, gy, n_rows, N, K, A, rowmap, topk, offsets, elist, ecount, wa,
+                                         wb, out, s);
 }
 
 hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* A, const int32_t* rowmap,

@@ -919,15 +919,15 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
                                     (const bf16*)w3, (bf16*)act, nullptr, s);
     if (err != hipSuccess) return err;
     if (small) {
-        err = launch_small_experts(true, n_rows, F, d, A, rowmap, topk, offsets, small_list, small_count, w1, w3,
-                                   act, s);
+        err = launch_small_experts(true, E, n_rows, F, d, A, rowmap, topk, offsets, small_list, small_count, w1,
+                                   w3, act, s);
         if (err != hipSuccess) return err;
     }
     err = launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
                                      (const bf16*)act, nullptr, 1, mt_count, mt_expert, mt_row0, offsets,
                                      (const bf16*)w2, nullptr, (bf16*)h, part, s);
     if (err != hipSuccess || !small) return err;
-    return launch_small_experts(false, n_rows, d, F, act, nullptr, 1, offsets, small_list, small_count, w2,
+    return launch_small_experts(false, E, n_rows, d, F, act, nullptr, 1, offsets, small_list, small_count, w2,
                                 nullptr, h, s);
 }
 

@@ -195,7 +195,13 @@ __global__ __launch_bounds__(256) void psum_reduce_kernel(int nblk, int E,
     if (e >= E) return;
     const int lane = lane_id();
     double s = 0.0;
-    for (int b = lane; b < nblk; b += kWave) s += (double)part[(size_t)b * E + e];
+    for (int b0 = lane; b0 < nblk; b0 += 8 * kWave) {  // eight loads in flight, added in block order
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = b0 + q * kWave < nblk ? part[(size_t)(b0 + q * kWave) * E + e] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += (double)v[q];
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     if (lane == 0) prob_sum[e] = (float)s;

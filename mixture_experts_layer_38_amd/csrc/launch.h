@@ -65,9 +65,9 @@ hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* 
 // the weight-streaming decode kernel (the tiled GEMM skips them).
 constexpr int DC_SMALL_ROWS = 32;
 // elist[0 .. *ecount): the small experts (device memory, written by the tile plan).
-hipError_t launch_small_experts(bool gated, int n_rows, int N, int K, const void* A, const int32_t* rowmap,
-                                int topk, const int32_t* offsets, const int32_t* elist, const int32_t* ecount,
-                                const void* wa, const void* wb, void* out, hipStream_t s);
+hipError_t launch_small_experts(bool gated, int E, int n_rows, int N, int K, const void* A,
+                                const int32_t* rowmap, int topk, const int32_t* offsets, const int32_t* elist,
+                                const int32_t* ecount, const void* wa, const void* wb, void* out, hipStream_t s);
 // ---- router regularisers ----------------------------------------------------
 size_t router_losses_ws_bytes(int T, int E);
 hipError_t launch_router_losses(int T, int E, int K, const float* logits, const float* bias,
