@@ -56,6 +56,7 @@ class Oracle:
         lib.oracle_z_loss.restype = ctypes.c_double
         lib.oracle_aux_topk.argtypes = [i64, i64, i64, vp, vp, vp]
         lib.oracle_aux_topk.restype = ctypes.c_double
+        lib.oracle_combine_concat.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp]
         for name in ("oracle_router_logits", "oracle_route", "oracle_dispatch",
                      "oracle_expert", "oracle_layer_output", "oracle_bias_update"):
             getattr(lib, name).restype = None
@@ -164,6 +165,22 @@ class Oracle:
         probs = np.ascontiguousarray(probs, np.float64)
         T, E = probs.shape
         return float(self.lib.oracle_aux_topk(T, E, ids.shape[1], _p(counts), _p(ids), _p(probs)))
+
+    def combine_concat(self, h: np.ndarray, assign_row: np.ndarray, w_cat: np.ndarray, dtype: str = "f32") -> np.ndarray:
+        """y [T, d_out] (float64) = w_cat . concat over slots of h[assign_row[t, k]];
+        h [S, d] and w_cat [d_out, K*d] as float32 arrays, or uint16 bf16 bits
+        with dtype="bf16"; assign_row [T, K] int32 (-1 = dropped)."""
+        assign_row = np.ascontiguousarray(assign_row, np.int32)
+        T, K = assign_row.shape
+        dt = BF16 if dtype == "bf16" else F32
+        h = np.ascontiguousarray(h, np.uint16 if dt == BF16 else np.float32)
+        w_cat = np.ascontiguousarray(w_cat, np.uint16 if dt == BF16 else np.float32)
+        d = h.shape[1]
+        d_out = w_cat.shape[0]
+        assert w_cat.shape[1] == K * d
+        y = np.zeros((T, d_out), np.float64)
+        self.lib.oracle_combine_concat(T, K, d, d_out, dt, _p(h), _p(assign_row), _p(w_cat), _p(y))
+        return y
 
     def bias_update(self, counts: np.ndarray, T: int, K: int, alpha: float,
                     bias: np.ndarray) -> np.ndarray:

@@ -273,3 +273,24 @@ double oracle_aux_topk(int64_t T, int64_t E, int64_t K, const int32_t* counts,
     }
     return sum_fp * (double)E;
 }
+
+/* [NOTES] §2.3, the combine that concatenates the K expert outputs of a token
+ * in slot order and applies one linear layer to the concatenation:
+ *   y[t, o] = sum over slots k, features i of  h[assign_row[t,k], i] * Wc[o, k*d + i].
+ * A slot dropped by capacity (assign_row < 0) contributes a zero block. */
+void oracle_combine_concat(int64_t T, int64_t K, int64_t d, int64_t d_out, int dtype,
+                           const void* h, const int32_t* assign_row, const void* w_cat, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t o = 0; o < d_out; ++o) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int32_t row = assign_row[t * K + k];
+                if (row < 0) continue; /* dropped slot: a block of zeros */
+                for (int64_t i = 0; i < d; ++i)
+                    acc += value_at(h, dtype, (int64_t)row * d + i) * value_at(w_cat, dtype, o * K * d + k * d + i);
+            }
+            y[t * d_out + o] = acc;
+        }
+    }
+}

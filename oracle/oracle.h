@@ -80,4 +80,11 @@ double oracle_aux_topk(int64_t T, int64_t E, int64_t K, const int32_t* counts,
 /* Number of OpenMP threads the oracle runs with. */
 int oracle_num_threads(void);
 
+/* Concatenation combine ([NOTES] §2.3): y[t] = Wc . concat_k h[assign_row[t,k]]
+ * (slot order; a dropped slot is a zero block).  h [S,d], Wc [d_out, K*d]
+ * (out-features-major, like a linear layer's weight), assign_row [T,K],
+ * y [T, d_out] double. */
+void oracle_combine_concat(int64_t T, int64_t K, int64_t d, int64_t d_out, int dtype,
+                           const void* h, const int32_t* assign_row, const void* w_cat, double* y);
+
 #endif

@@ -514,4 +514,63 @@ def pin_select_only_properties(orc):
     assert np.array_equal(a[0], b[0]) and np.allclose(a[1], b[1], rtol=0, atol=1e-15)
 
 
+# --------------------------------------------------------------------------
+# concatenation combine (notes §2.3)
+# --------------------------------------------------------------------------
+
+def _concat_case(r, T, K, d, d_out, drop=0.25):
+    S = T * K
+    h = r.standard_normal((S, d)).astype(np.float32)
+    rows = r.permutation(S).astype(np.int32).reshape(T, K)
+    rows[r.random((T, K)) < drop] = -1
+    w = r.standard_normal((d_out, K * d)).astype(np.float32)
+    return h, rows, w
+
+
+def pin_concat_identity_blocks(orc):
+    """Wc = [c_0 I | c_1 I | ...] turns the concatenation combine into the
+    weighted sum  y[t] = sum over kept slots of c_k h_k (numpy, row by row)."""
+    r = _rng(31)
+    T, K, d = 9, 3, 6
+    h, rows, _ = _concat_case(r, T, K, d, d)
+    c = np.array([1.0, -0.5, 2.0], np.float32)
+    w = np.concatenate([ck * np.eye(d, dtype=np.float32) for ck in c], axis=1)
+    want = np.zeros((T, d))
+    for t in range(T):
+        for k in range(K):
+            if rows[t, k] >= 0:
+                want[t] += float(c[k]) * h[rows[t, k]].astype(np.float64)
+    np.testing.assert_allclose(orc.combine_concat(h, rows, w), want, rtol=0, atol=1e-12)
+
+
+def pin_concat_single_slot_is_a_linear_layer(orc):
+    """K = 1 with nothing dropped: y = h[rows] Wc^T, numpy's float64 matmul."""
+    r = _rng(32)
+    h, rows, w = _concat_case(r, 11, 1, 7, 5, drop=0.0)
+    want = h[rows[:, 0]].astype(np.float64) @ w.astype(np.float64).T
+    np.testing.assert_allclose(orc.combine_concat(h, rows, w), want, rtol=1e-13, atol=1e-13)
+
+
+def pin_concat_library(orc):
+    """The concatenated rows (zero blocks for dropped slots) times Wc^T, by
+    numpy in float64, for several shapes including d_out != d."""
+    r = _rng(33)
+    for T, K, d, d_out in ((5, 2, 4, 4), (8, 4, 3, 7), (3, 8, 16, 2)):
+        h, rows, w = _concat_case(r, T, K, d, d_out)
+        x = np.zeros((T, K * d))
+        for t in range(T):
+            for k in range(K):
+                if rows[t, k] >= 0:
+                    x[t, k * d:(k + 1) * d] = h[rows[t, k]]
+        np.testing.assert_allclose(orc.combine_concat(h, rows, w), x @ w.astype(np.float64).T,
+                                   rtol=1e-12, atol=1e-12)
+
+
+def pin_concat_all_dropped(orc):
+    """Every slot dropped: y = 0 exactly."""
+    r = _rng(34)
+    h, rows, w = _concat_case(r, 4, 2, 5, 5, drop=1.0)
+    assert np.all(orc.combine_concat(h, rows, w) == 0.0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

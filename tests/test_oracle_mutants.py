@@ -45,6 +45,11 @@ MUTANTS = [
      "chosen += probs[t * E + e] / (double)K;"),
     ("top-K aux over slots", "sum_fp += frac * (chosen / (double)T);", "sum_fp += frac * (chosen / (double)(T * K));"),
     ("top-K aux without the N factor", "return sum_fp * (double)E;", "return sum_fp;"),
+    ("concat weight transposed", "value_at(w_cat, dtype, o * K * d + k * d + i)",
+     "value_at(w_cat, dtype, (k * d + i) * d_out + o)"),
+    ("concat dropped slot read", "if (row < 0) continue; /* dropped slot: a block of zeros */", ""),
+    ("concat slots reversed", "const int32_t row = assign_row[t * K + k];",
+     "const int32_t row = assign_row[t * K + (K - 1 - k)];"),
 ]
 
 
