@@ -162,6 +162,65 @@ def time_chunked(cfg, layer, x, bias, chunk: int, steps: int):
             "workspace_bytes": ws_bytes, "workspace_bytes_unchunked": moe.moe_workspace_size(p)}
 
 
+def _event_ms(fn, reps: int) -> float:
+    """Mean milliseconds of fn() over reps back-to-back calls (HIP events on the current stream)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def time_variants(cfg, layer, x, bias, steps: int, concat: bool = True):
+    """The layer's other forms on the same resident batch: the routing
+    variants (bias for selection only, unweighted mean), the router
+    regularisers, and the concatenation combine (K outputs concatenated, one
+    linear layer [d, K*d]) with its roofline."""
+    import torch
+    import mixture_experts_layer_38_amd as moe
+    from mixture_experts_layer_38_amd.layer import MoELayer
+    out = {}
+    y = torch.empty((cfg.T, cfg.d), dtype=layer.torch_dtype, device="cuda")
+    for name, flags in (("bias_select_only", moe.MOE_FLAG_BIAS_SELECT_ONLY), ("mean_combine", moe.MOE_FLAG_COMBINE_MEAN)):
+        v = MoELayer(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, cfg.dtype, layer.w_router, layer.w1, layer.w3, layer.w2,
+                     cfg.capacity, flags=flags)
+        ms = _event_ms(lambda: v.forward(x, bias, y=y), steps)
+        out[name] = {"ms_per_step": ms, "value": cfg.T / (ms * 1e-3), "unit": "tokens/s"}
+    dbg = layer.alloc_debug()
+    layer.forward(x, bias, y=y, dbg=dbg)
+    p = layer.p
+    ws = torch.empty(moe.moe_router_losses_workspace_size(p), dtype=torch.uint8, device="cuda")
+    z = torch.empty(1, dtype=torch.float32, device="cuda")
+    a = torch.empty(1, dtype=torch.float32, device="cuda")
+    ms = _event_ms(lambda: moe.moe_router_losses(p, dbg["logits"], bias, dbg["topk_ids"], dbg["counts"], z, a, ws),
+                   steps)
+    out["router_losses"] = {"us_per_call": ms * 1e3}
+    if concat:
+        g = torch.Generator(device="cuda").manual_seed(11)
+        S, dk = cfg.T * cfg.K, cfg.K * cfg.d
+        h = torch.randn(S, cfg.d, device="cuda", generator=g).to(layer.torch_dtype)
+        w_cat = (torch.randn(cfg.d, dk, device="cuda", generator=g) / dk ** 0.5).to(layer.torch_dtype)
+        cws = torch.empty(moe.moe_combine_concat_workspace_size(p), dtype=torch.uint8, device="cuda")
+        ms = _event_ms(lambda: moe.moe_combine_concat(p, h, dbg["assign_row"], w_cat, y, cws), steps)
+        es = h.element_size()
+        nbytes = (cfg.d * dk + S * cfg.d + cfg.T * cfg.d) * es
+        flops = 2.0 * cfg.T * dk * cfg.d
+        rec = {"us_per_call": ms * 1e3, "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+        if cfg.T <= 64:
+            rec["roofline"] = {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        else:
+            rec["roofline"] = {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
+                               "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
+        out["concat_combine"] = rec
+    return out
+
+
 def cpu_baseline(cfg, inp, min_seconds: float = 10.0, max_reps: int = 200):
     """The CPU oracle (fp64, OpenMP on this host's cores) on the same workload:
     whole forward passes of the first min(T, 32) tokens (routing, grouping,
@@ -197,7 +256,10 @@ def main():
     ap.add_argument("--prefill-chunk", type=int, default=2048)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="launch every pass eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-variants", action="store_true", help="skip the routing/combine variants and router losses")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph per pass instead of launching eagerly "
+                         "(measured about 1% slower on the decode step)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path "
@@ -219,7 +281,7 @@ def main():
     bias = None if inp["logit_bias"] is None else torch.from_numpy(inp["logit_bias"]).cuda()
     print("[bench] timing", file=sys.stderr, flush=True)
     wall, k_ms, counts, kept = time_workload(cfg, layer, x, bias, args.steps, args.warmup, "ffn_gate_up",
-                                              not args.no_graph)
+                                              args.graph)
     ms_step = wall / args.steps * 1e3
     tok_s = cfg.T * args.steps / wall
     gb, gf = gate_up_algorithmic(cfg, kept)
@@ -233,7 +295,7 @@ def main():
         "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} K={cfg.K} "
                                f"F={cfg.F} {cfg.dtype}", "T": cfg.T, "d_model": cfg.d,
                    "experts": cfg.E, "top_k": cfg.K, "d_ff": cfg.F, "capacity": cfg.capacity,
-                   "launch": "eager" if args.no_graph else "hip graph replay"},
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel_ms": k_ms, "algorithmic_bytes": gb},
@@ -241,6 +303,9 @@ def main():
                   "algorithmic_bytes": lb, "algorithmic_flops": lf,
                   "counts": counts.tolist()},
     }
+    if not args.no_variants:
+        print("[bench] timing the variants", file=sys.stderr, flush=True)
+        result["variants"] = time_variants(cfg, layer, x, bias, 20, concat=cfg.dtype == "bf16")
     if not args.no_prefill and cfg.name == "mixtral_decode":
         pcfg = CONFIGS["mixtral_prefill"]
         pin = datagen.make_inputs(pcfg, with_experts=False)
@@ -250,7 +315,7 @@ def main():
         pb = torch.from_numpy(pin["logit_bias"]).cuda()
         print("[bench] timing prefill", file=sys.stderr, flush=True)
         pwall, pk_ms, pcounts, pkept = time_workload(pcfg, player, px, pb, args.prefill_steps, 2,
-                                                     "ffn_gate_up", not args.no_graph)
+                                                     "ffn_gate_up", args.graph)
         pgb, pgf = gate_up_algorithmic(pcfg, pkept)
         plb, plf = layer_algorithmic(pcfg, pkept)
         pms = pwall / args.prefill_steps * 1e3
@@ -266,6 +331,8 @@ def main():
             "counts": pcounts.tolist(),
             "chunked": time_chunked(pcfg, player, px, pb, args.prefill_chunk, args.prefill_steps),
         }
+        if not args.no_variants:
+            result["prefill"]["variants"] = time_variants(pcfg, player, px, pb, 3)
         del player, px
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -226,6 +226,21 @@ moe_status moe_aux_loss(const moe_problem* p, const int32_t* counts, const float
 moe_status moe_bias_update(const moe_problem* p, const int32_t* counts, float alpha,
                            float* bias, void* stream);
 
+/* Concatenation combine: [NOTES] §2.3 (the alternative to the weighted sum:
+ * concatenate the K expert outputs of a token, then one linear layer).
+ *   y[t] = W_cat . concat over k = 0..K-1 of h[assign_row[t,k]]
+ * A slot dropped by capacity (assign_row = -1) gives a block of zeros; the
+ * routing weights are not used.
+ *   h [S,d] grouped expert outputs (as moe_expert_ffn writes them, layer
+ *   dtype), assign_row [T,K] int32 (moe_dispatch), W_cat [d, K*d] (layer
+ *   dtype, out-features-major like a linear layer's weight), y [T,d] (layer
+ *   dtype; bf16 accumulates in fp32 and rounds once).
+ *   ws: moe_combine_concat_workspace_size bytes, 16-byte aligned.  Sums run
+ *   in a fixed order (run-to-run identical). */
+moe_status moe_combine_concat_workspace_size(const moe_problem* p, size_t* bytes);
+moe_status moe_combine_concat(const moe_problem* p, const void* h, const int32_t* assign_row,
+                              const void* w_cat, void* y, void* ws, size_t ws_bytes, void* stream);
+
 /* Router regularisers: [NOTES] §3.2.
  *   z_loss   = (1/T) sum_t (log sum_e exp(logits[t,e]))^2 over the router
  *              scores as moe_route writes them (before the bias);

@@ -65,10 +65,12 @@ def _lib():
         "moe_expert_ffn_workspace_size": [P, ctypes.POINTER(sz)],
         "moe_workspace_size": [P, ctypes.POINTER(sz)],
         "moe_router_losses_workspace_size": [P, ctypes.POINTER(sz)],
+        "moe_combine_concat_workspace_size": [P, ctypes.POINTER(sz)],
         "moe_forward_chunked_workspace_size": [P, ctypes.c_int32, ctypes.POINTER(sz)],
         "moe_forward_chunked": [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.POINTER(MoEDebugOut), vp, sz, vp],
         "moe_router_losses": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_combine_concat": [P, vp, vp, vp, vp, vp, sz, vp],
         "moe_route": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_dispatch": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_expert_ffn": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -216,6 +218,16 @@ def moe_aux_loss(p, counts, prob_sum, aux, stream=None):
                                _stream(stream)), "moe_aux_loss")
 
 
+def moe_combine_concat_workspace_size(p: MoEProblem) -> int:
+    return _size(_lib().moe_combine_concat_workspace_size, p)
+
+
+def moe_combine_concat(p, h, assign_row, w_cat, y, ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib().moe_combine_concat(ctypes.byref(p), _ptr(h), _ptr(assign_row), _ptr(w_cat), _ptr(y),
+                                     _ptr(ws), ws_bytes, _stream(stream)), "moe_combine_concat")
+
+
 def moe_router_losses(p, logits, logit_bias, topk_ids, counts, z_loss, aux_topk, ws, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib().moe_router_losses(ctypes.byref(p), _ptr(logits), _ptr(logit_bias), _ptr(topk_ids),
@@ -255,6 +267,7 @@ __all__ = [
     "moe_workspace_size", "moe_route_workspace_size", "moe_dispatch_workspace_size",
     "moe_expert_ffn_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
     "moe_forward", "moe_forward_chunked", "moe_forward_chunked_workspace_size", "moe_aux_loss", "moe_bias_update", "moe_router_losses",
+    "moe_combine_concat", "moe_combine_concat_workspace_size",
     "moe_router_losses_workspace_size", "moe_set_kernel_timer",
     "moe_kernel_timer_count",
 ]

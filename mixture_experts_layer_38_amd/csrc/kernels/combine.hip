@@ -45,6 +45,76 @@ __global__ __launch_bounds__(256) void combine_kernel(int n_tok, int K, int d,
     store16(y + (size_t)t * d + c, outv);
 }
 
+// Concatenation combine, first half: X[t] = concat over slots k of
+// h[assign_row[t,k]] (a zero block for a dropped slot), one thread per 16-byte
+// vector; block 0 also writes the one-group row offsets {0, T} that the linear
+// layer's GEMM reads.
+template <typename T>
+__global__ __launch_bounds__(256) void concat_gather_kernel(int n_tok, int K, int d,
+                                                           const T* __restrict__ h,
+                                                           const int32_t* __restrict__ assign_row,
+                                                           T* __restrict__ x, int32_t* __restrict__ offs) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int per_tok = K * d / VEC;
+    if (blockIdx.x == 0 && threadIdx.x < 2) offs[threadIdx.x] = threadIdx.x == 0 ? 0 : n_tok;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)n_tok * per_tok) return;
+    const int t = (int)(i / per_tok);
+    const int c = (int)(i - (size_t)t * per_tok) * VEC;  // column of X
+    const int k = c / d;
+    const int r = assign_row[(size_t)t * K + k];
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 v = (unsigned)r < (unsigned)(n_tok * K) ? load16(h + (size_t)r * d + (c - k * d)) : z;
+    store16(x + (size_t)t * K * d + c, v);
+}
+
+// fp32 linear layer: y[t, o] = sum_j x[t, j] * W[o, j], one thread per output.
+__global__ __launch_bounds__(256) void linear_f32_kernel(int n_tok, int n_out, int n_in,
+                                                        const float* __restrict__ x,
+                                                        const float* __restrict__ w,
+                                                        float* __restrict__ y) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)n_tok * n_out) return;
+    const int t = (int)(i / n_out);
+    const int o = (int)(i - (size_t)t * n_out);
+    const float* xr = x + (size_t)t * n_in;
+    const float* wr = w + (size_t)o * n_in;
+    float s = 0.0f;
+    for (int j = 0; j < n_in; ++j) s = fmaf(xr[j], wr[j], s);
+    y[i] = s;
+}
+
+size_t combine_concat_ws_bytes(int T, int K, int d, int dtype) {
+    const size_t es = dtype == MOE_DTYPE_F32 ? 4 : 2;
+    size_t b = align_up((size_t)T * K * d * es, 256) + 256;
+    if (dtype == MOE_DTYPE_BF16) b += linear_ws_bytes(T, d);
+    return b;
+}
+
+hipError_t launch_combine_concat(int T, int K, int d, int dtype, const void* h, const int32_t* assign_row,
+                                 const void* w_cat, void* y, void* ws, hipStream_t s) {
+    const size_t es = dtype == MOE_DTYPE_F32 ? 4 : 2;
+    char* base = reinterpret_cast<char*>(ws);
+    void* x = base;
+    int32_t* offs = reinterpret_cast<int32_t*>(base + align_up((size_t)T * K * d * es, 256));
+    void* lws = base + align_up((size_t)T * K * d * es, 256) + 256;
+    const size_t nvec = (size_t)T * K * d * es / 16;
+    const unsigned grid = (unsigned)((nvec + 255) / 256);
+    if (dtype == MOE_DTYPE_F32) {
+        concat_gather_kernel<float><<<grid, 256, 0, s>>>(T, K, d, (const float*)h, assign_row, (float*)x, offs);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const size_t n = (size_t)T * d;
+        linear_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(T, d, K * d, (const float*)x,
+                                                                       (const float*)w_cat, (float*)y);
+        return hipGetLastError();
+    }
+    concat_gather_kernel<bf16><<<grid, 256, 0, s>>>(T, K, d, (const bf16*)h, assign_row, (bf16*)x, offs);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_linear(T, d, K * d, x, offs, w_cat, y, lws, s);
+}
+
 __global__ __launch_bounds__(1024) void aux_kernel(int T, int K, int E,
                                                   const int32_t* __restrict__ counts,
                                                   const float* __restrict__ prob_sum,

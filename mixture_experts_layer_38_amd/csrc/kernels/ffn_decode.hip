@@ -264,6 +264,20 @@ hipError_t launch_small_experts(bool gated, int E, int n_rows, int N, int K, con
                                          wb, out, s);
 }
 
+// One group of at most 64 rows against W [N, K]: one pass of 64 token rows
+// over each strip of 32 weight rows.
+hipError_t launch_linear_small(int n_rows, int N, int K, const void* A, const int32_t* offs, const void* w,
+                               void* out, hipStream_t s) {
+    dim3 g((N + 2 * DC_ROWS - 1) / (2 * DC_ROWS), 1);
+    if (K % DC_KCH == 0)
+        ffn_decode_kernel<false, 1, 4, true, 2><<<g, DC_WAVES * kWave, 0, s>>>(
+            n_rows, N, K, (const bf16*)A, nullptr, 1, offs, (const bf16*)w, nullptr, (bf16*)out);
+    else
+        ffn_decode_kernel<false, 1, 4, false, 2><<<g, DC_WAVES * kWave, 0, s>>>(
+            n_rows, N, K, (const bf16*)A, nullptr, 1, offs, (const bf16*)w, nullptr, (bf16*)out);
+    return hipGetLastError();
+}
+
 hipError_t launch_ffn_decode(int n_rows, int E, int d, int F, const void* A, const int32_t* rowmap,
                              int topk, const int32_t* offsets, const void* w1, const void* w3,
                              const void* w2, void* act, void* h, hipStream_t s) {

@@ -931,4 +931,32 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
                                 nullptr, h, s);
 }
 
+// A plain linear layer (one group of n_rows rows) on the second GEMM's
+// kernels: the tile plan for E = 1, then the tiled GEMM (with its last-round
+// split).  Up to 64 rows stream W through the decode kernel instead.
+hipError_t launch_linear_small(int n_rows, int N, int K, const void* A, const int32_t* offs, const void* w,
+                               void* out, hipStream_t s);
+
+size_t linear_ws_bytes(int n_rows, int N) { return prefill_ws_bytes(n_rows, 1, N); }
+
+hipError_t launch_linear(int n_rows, int N, int K, const void* x, const int32_t* offs, const void* w, void* y,
+                         void* ws, hipStream_t s) {
+    if (n_rows <= 64) return launch_linear_small(n_rows, N, K, x, offs, w, y, s);
+    const int max_mt = prefill_max_mtiles(n_rows, 1);
+    const int bm = (K % PF_BK != 0) ? 256 : (n_rows >= 512 ? 256 : 128);
+    int32_t* mt_count = reinterpret_cast<int32_t*>(ws);
+    int32_t* mt_expert = mt_count + 1;
+    int32_t* mt_row0 = mt_expert + max_mt;
+    int32_t* small_count = mt_row0 + max_mt;
+    int32_t* small_list = small_count + 1;
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + prefill_plan_bytes(n_rows, 1));
+    ffn_plan_kernel<<<1, 1024, 0, s>>>(1, max_mt, bm, 0, offs, mt_count, mt_expert, mt_row0, small_count,
+                                       small_list);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_prefill_gemm<false>(n_rows, N, K, (N + PF_BN - 1) / PF_BN, max_mt, bm, (const bf16*)x, nullptr,
+                                      1, mt_count, mt_expert, mt_row0, offs, (const bf16*)w, nullptr, (bf16*)y,
+                                      part, s);
+}
+
 }  // namespace moe

@@ -74,7 +74,19 @@ hipError_t launch_router_losses(int T, int E, int K, const float* logits, const 
                                 const int32_t* ids, const int32_t* counts, float* z_loss,
                                 float* aux_topk, void* ws, hipStream_t s);
 
+// ---- linear layer on the expert-GEMM kernels ---------------------------------
+// y[t, o] = sum_j x[t, j] * W[o, j] for t < n_rows (bf16, fp32 accumulation):
+// x [n_rows, K], W [N, K], y [n_rows, N]; offs = {0, n_rows} in device memory
+// (the kernels see one group of rows).  Small n_rows stream W once through the
+// decode kernel, larger ones use the tiled GEMM.  ws: linear_ws_bytes.
+size_t linear_ws_bytes(int n_rows, int N);
+hipError_t launch_linear(int n_rows, int N, int K, const void* x, const int32_t* offs, const void* w,
+                         void* y, void* ws, hipStream_t s);
 // ---- combine / aux / bias --------------------------------------------------
+// Concatenation combine: y[t] = W_cat . concat over slots of h[assign_row[t,k]].
+size_t combine_concat_ws_bytes(int T, int K, int d, int dtype);
+hipError_t launch_combine_concat(int T, int K, int d, int dtype, const void* h, const int32_t* assign_row,
+                                 const void* w_cat, void* y, void* ws, hipStream_t s);
 hipError_t launch_combine(int T, int K, int d, int dtype, const void* h,
                           const int32_t* assign_row, const float* w, void* y, hipStream_t s);
 hipError_t launch_aux(int T, int K, int E, const int32_t* counts, const float* prob_sum,

@@ -409,6 +409,28 @@ moe_status moe_aux_loss(const moe_problem* p, const int32_t* counts, const float
                                  (hipStream_t)stream));
 }
 
+moe_status moe_combine_concat_workspace_size(const moe_problem* p, size_t* bytes) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = combine_concat_ws_bytes(p->T, p->top_k, p->d_model, p->dtype);
+    return MOE_OK;
+}
+
+moe_status moe_combine_concat(const moe_problem* p, const void* h, const int32_t* assign_row,
+                              const void* w_cat, void* y, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    REQUIRE(h);
+    REQUIRE(assign_row);
+    REQUIRE(w_cat);
+    REQUIRE(y);
+    if (!ws || ws_bytes < combine_concat_ws_bytes(p->T, p->top_k, p->d_model, p->dtype)) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_combine_concat(p->T, p->top_k, p->d_model, p->dtype, h, assign_row, w_cat, y, ws,
+                                            (hipStream_t)stream));
+}
+
 moe_status moe_router_losses_workspace_size(const moe_problem* p, size_t* bytes) {
     moe_status st = check_problem(p);
     if (st != MOE_OK) return st;

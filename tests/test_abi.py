@@ -124,6 +124,20 @@ def test_router_losses_rejects_bad_arguments():
     assert lib.moe_router_losses(P, A, None, None, A, A, A, A, ws, None) == INVALID
 
 
+def test_combine_concat_rejects_bad_arguments():
+    lib = moe.load()
+    p = moe.problem(64, 128, 8, 2, 256, "bf16")
+    P = ctypes.byref(p)
+    ws = moe.moe_combine_concat_workspace_size(p)
+    assert ws >= 64 * 2 * 128 * 2  # the concatenated rows at least
+    assert moe.moe_combine_concat_workspace_size(moe.problem(4096, 128, 8, 2, 256, "bf16")) > ws
+    assert lib.moe_combine_concat(P, None, A, A, A, A, ws, None) == INVALID
+    assert lib.moe_combine_concat(P, A, A, None, A, A, ws, None) == INVALID
+    assert lib.moe_combine_concat(P, A, A, A, A, A, ws - 1, None) == WORKSPACE
+    assert lib.moe_combine_concat(P, A, A, A, A, MIS, ws, None) == ALIGN
+    assert lib.moe_combine_concat(P, MIS, A, A, A, A, ws, None) == ALIGN
+
+
 def test_timer_hook_bookkeeping():
     lib = moe.load()
     n = ctypes.c_int(-1)
