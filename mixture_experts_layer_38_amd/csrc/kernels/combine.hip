@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(int n_tok, int n_out, i
 size_t combine_concat_ws_bytes(int T, int K, int d, int dtype) {
     const size_t es = dtype == MOE_DTYPE_F32 ? 4 : 2;
     size_t b = align_up((size_t)T * K * d * es, 256) + 256;
-    if (dtype == MOE_DTYPE_BF16) b += linear_ws_bytes(T, d);
+    if (dtype == MOE_DTYPE_BF16) b += linear_ws_bytes(T, d, K * d);
     return b;
 }
 

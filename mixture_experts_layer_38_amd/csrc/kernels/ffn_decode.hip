@@ -17,6 +17,8 @@
 // from L2 just before their use.  Partial sums meet in LDS, where the
 // fixed-order sum and the epilogue (SiLU(g1) * g3 for gate/up) run.  Experts
 // with no rows are skipped without touching their weights.
+#include <algorithm>
+
 #include "../device_common.h"
 #include "../launch.h"
 
@@ -37,11 +39,14 @@ __device__ __forceinline__ u32x4 load16_masked(const bf16* row, int k, int K) {
 }
 
 // The rows of expert e against this workgroup's strip of weight rows.
-template <bool GATED, int CPI, int NCB, bool ALIGNED, int R>
+// K is the reduction length and ldk the row stride of A and of the weights
+// (ldk > K when the caller splits the reduction).  PART writes the fp32 sums
+// to part [n_rows, N] instead of bf16 to out.
+template <bool GATED, int CPI, int NCB, bool ALIGNED, int R, bool PART = false>
 __device__ __forceinline__ void ffn_decode_group(
     int e, int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
     const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
-    bf16* __restrict__ out) {
+    bf16* __restrict__ out, int ldk, float* __restrict__ part = nullptr) {
     constexpr int NG = GATED ? 2 : 1;
     constexpr int NS = 4 * CPI;          // 32-wide slices per chunk
     constexpr int KCH = DC_KCH * CPI;  // k per chunk
@@ -64,8 +69,8 @@ __device__ __forceinline__ void ffn_decode_group(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int wrow = min(n0 + DC_ROWS * r + rl, N - 1);
-        wa[r] = Wa + ((size_t)e * N + wrow) * K;
-        wb[r] = GATED ? Wb + ((size_t)e * N + wrow) * K : nullptr;
+        wa[r] = Wa + ((size_t)e * N + wrow) * ldk;
+        wb[r] = GATED ? Wb + ((size_t)e * N + wrow) * ldk : nullptr;
     }
     const int kl = g * 8;  // this lane's k offset inside each 32-wide slice
 
@@ -82,7 +87,7 @@ __device__ __forceinline__ void ffn_decode_group(
         const bf16* arow[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-            arow[cb] = A + (size_t)src_row(rowmap, topk, r0 + p0 + min(cb * 16 + rl, mp - 1)) * K;
+            arow[cb] = A + (size_t)src_row(rowmap, topk, r0 + p0 + min(cb * 16 + rl, mp - 1)) * ldk;
 
         // Double buffer in registers: the weight loads of chunk c + 1 are issued
         // after the token loads of chunk c, so waiting for the tokens of chunk c
@@ -171,7 +176,14 @@ __device__ __forceinline__ void ffn_decode_group(
                         }
                         v[i] = GATED ? silu(s0) * s1 : s0;
                     }
-                    if (tcol < mp) {
+                    if (PART && tcol < mp) {
+                        // N is a multiple of 4 here (the caller checks), so
+                        // the four values are one aligned 16-byte store
+                        const int col = n0 + DC_ROWS * r + g * 4;
+                        if (col < N)
+                            *reinterpret_cast<f32x4*>(part + (size_t)(r0 + p0 + tcol) * N + col) =
+                                f32x4{v[0], v[1], v[2], v[3]};
+                    } else if (tcol < mp) {
                         const int col = n0 + DC_ROWS * r + g * 4;
                         bf16* o = out + (size_t)(r0 + p0 + tcol) * N + col;
                         if (col + 3 < N) {
@@ -194,7 +206,8 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
     int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
     const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
     bf16* __restrict__ out) {
-    ffn_decode_group<GATED, CPI, NCB, ALIGNED, R>(blockIdx.y, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out);
+    ffn_decode_group<GATED, CPI, NCB, ALIGNED, R>(blockIdx.y, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out,
+                                                  K);
 }
 
 // The experts listed in elist[0 .. *ecount) (small groups of a large batch),
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_small_experts_kernel(
     const int cnt = *ecount;
     for (int i = blockIdx.y; i < cnt; i += gridDim.y)
         ffn_decode_group<GATED, CPI, NCB, ALIGNED, R>(elist[i], n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb,
-                                                      out);
+                                                      out, K);
 }
 
 template <bool ALIGNED>
@@ -265,9 +278,77 @@ hipError_t launch_small_experts(bool gated, int E, int n_rows, int N, int K, con
 }
 
 // One group of at most 64 rows against W [N, K]: one pass of 64 token rows
-// over each strip of 32 weight rows.
+// over each strip of 32 weight rows.  With few strips the reduction is split
+// into gridDim.y parts of kp values (a multiple of the 128-value chunk), each
+// writing fp32 sums to its own slice of part; linear_part_reduce_kernel then
+// adds the parts in index order, so the result does not depend on timing.
+// NCB 16-row token blocks per pass: 2 for up to 32 rows (fewer registers,
+// three workgroups per CU), 4 for up to 64.
+template <bool ALIGNED, int NCB>
+__global__ __launch_bounds__(DC_WAVES * kWave) void linear_part_kernel(
+    int n_rows, int N, int K, int kp, const bf16* __restrict__ A, const int32_t* __restrict__ offs,
+    const bf16* __restrict__ W, float* __restrict__ part) {
+    const int kb = blockIdx.y * kp;
+    ffn_decode_group<false, 1, NCB, ALIGNED, 2, true>(0, n_rows, N, min(kp, K - kb), A + kb, nullptr, 1, offs,
+                                                      W + kb, nullptr, nullptr, K,
+                                                      part + (size_t)blockIdx.y * n_rows * N);
+}
+
+__global__ __launch_bounds__(256) void linear_part_reduce_kernel(int n, int parts, const float* __restrict__ part,
+                                                                 bf16* __restrict__ y) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+        float v = part[i];
+        for (int j = 1; j < parts; ++j) v += part[(size_t)j * n + i];
+        y[i] = (bf16)v;
+    }
+}
+
+// Parts of the reduction for a decode-sized linear layer: enough workgroups
+// to keep every CU streaming weights (about 1024), each wave keeping at least
+// eight chunks (shorter streams measured slower: a 64 MB weight took 20 us in
+// two parts of eight chunks per wave and 22 us in eight parts of two).
+// Returns the part length in *kp.
+static int linear_parts(int N, int K, int* kp) {
+    *kp = K;
+    if (N % 4 != 0) return 1;
+    const int gx = (N + 2 * DC_ROWS - 1) / (2 * DC_ROWS);
+    const int nch = (K + DC_KCH - 1) / DC_KCH;
+    int parts = std::min(std::min((1024 + gx - 1) / gx, nch / (8 * DC_WAVES)), LIN_MAX_PARTS);
+    if (parts < 1) parts = 1;
+    *kp = ((nch + parts - 1) / parts) * DC_KCH;
+    return (K + *kp - 1) / *kp;
+}
+
+size_t linear_small_ws_bytes(int n_rows, int N, int K) {
+    int kp;
+    const int parts = linear_parts(N, K, &kp);
+    return parts > 1 ? (size_t)parts * n_rows * N * sizeof(float) : 0;
+}
+
 hipError_t launch_linear_small(int n_rows, int N, int K, const void* A, const int32_t* offs, const void* w,
-                               void* out, hipStream_t s) {
+                               void* out, void* ws, hipStream_t s) {
+    int kp;
+    const int parts = linear_parts(N, K, &kp);
+    if (parts > 1) {
+        dim3 g((N + 2 * DC_ROWS - 1) / (2 * DC_ROWS), parts);
+        float* part = reinterpret_cast<float*>(ws);
+        const bf16* a = (const bf16*)A;
+        const bf16* wt = (const bf16*)w;
+        const bool al = K % DC_KCH == 0;
+        if (n_rows <= 32) {
+            if (al) linear_part_kernel<true, 2><<<g, DC_WAVES * kWave, 0, s>>>(n_rows, N, K, kp, a, offs, wt, part);
+            else linear_part_kernel<false, 2><<<g, DC_WAVES * kWave, 0, s>>>(n_rows, N, K, kp, a, offs, wt, part);
+        } else {
+            if (al) linear_part_kernel<true, 4><<<g, DC_WAVES * kWave, 0, s>>>(n_rows, N, K, kp, a, offs, wt, part);
+            else linear_part_kernel<false, 4><<<g, DC_WAVES * kWave, 0, s>>>(n_rows, N, K, kp, a, offs, wt, part);
+        }
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const int n = n_rows * N;
+        linear_part_reduce_kernel<<<std::max(1, std::min((n + 255) / 256, 1024)), 256, 0, s>>>(n, parts, part,
+                                                                                              (bf16*)out);
+        return hipGetLastError();
+    }
     dim3 g((N + 2 * DC_ROWS - 1) / (2 * DC_ROWS), 1);
     if (K % DC_KCH == 0)
         ffn_decode_kernel<false, 1, 4, true, 2><<<g, DC_WAVES * kWave, 0, s>>>(

@@ -934,14 +934,13 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
 // A plain linear layer (one group of n_rows rows) on the second GEMM's
 // kernels: the tile plan for E = 1, then the tiled GEMM (with its last-round
 // split).  Up to 64 rows stream W through the decode kernel instead.
-hipError_t launch_linear_small(int n_rows, int N, int K, const void* A, const int32_t* offs, const void* w,
-                               void* out, hipStream_t s);
-
-size_t linear_ws_bytes(int n_rows, int N) { return prefill_ws_bytes(n_rows, 1, N); }
+size_t linear_ws_bytes(int n_rows, int N, int K) {
+    return n_rows <= LIN_SMALL_ROWS ? linear_small_ws_bytes(n_rows, N, K) : prefill_ws_bytes(n_rows, 1, N);
+}
 
 hipError_t launch_linear(int n_rows, int N, int K, const void* x, const int32_t* offs, const void* w, void* y,
                          void* ws, hipStream_t s) {
-    if (n_rows <= 64) return launch_linear_small(n_rows, N, K, x, offs, w, y, s);
+    if (n_rows <= LIN_SMALL_ROWS) return launch_linear_small(n_rows, N, K, x, offs, w, y, ws, s);
     const int max_mt = prefill_max_mtiles(n_rows, 1);
     const int bm = (K % PF_BK != 0) ? 256 : (n_rows >= 512 ? 256 : 128);
     int32_t* mt_count = reinterpret_cast<int32_t*>(ws);

@@ -78,8 +78,14 @@ hipError_t launch_router_losses(int T, int E, int K, const float* logits, const 
 // y[t, o] = sum_j x[t, j] * W[o, j] for t < n_rows (bf16, fp32 accumulation):
 // x [n_rows, K], W [N, K], y [n_rows, N]; offs = {0, n_rows} in device memory
 // (the kernels see one group of rows).  Small n_rows stream W once through the
-// decode kernel, larger ones use the tiled GEMM.  ws: linear_ws_bytes.
-size_t linear_ws_bytes(int n_rows, int N);
+// decode kernel (its reduction split into parts when W has few rows), larger
+// ones use the tiled GEMM.  ws: linear_ws_bytes, 256-byte aligned.
+size_t linear_ws_bytes(int n_rows, int N, int K);
+constexpr int LIN_SMALL_ROWS = 64;
+constexpr int LIN_MAX_PARTS = 8;
+size_t linear_small_ws_bytes(int n_rows, int N, int K);
+hipError_t launch_linear_small(int n_rows, int N, int K, const void* A, const int32_t* offs, const void* w,
+                               void* out, void* ws, hipStream_t s);
 hipError_t launch_linear(int n_rows, int N, int K, const void* x, const int32_t* offs, const void* w,
                          void* y, void* ws, hipStream_t s);
 // ---- combine / aux / bias --------------------------------------------------

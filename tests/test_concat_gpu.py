@@ -3,7 +3,8 @@
 MoE notes §2.3: the K expert outputs of a token are concatenated in slot
 order (a slot dropped by capacity is a block of zeros) and passed through one
 linear layer W_cat [d, K*d].  Reduced cases compare every element; the
-Mixtral-sized cases (the decode batch through the weight-streaming kernel,
+Mixtral-sized cases (the decode batch through the weight-streaming kernel
+with its reduction split into parts,
 the prefill batch through the tiled GEMM with its last-round split) compare
 sampled tokens.
 """
@@ -72,6 +73,9 @@ def _run(orc, T, K, d, dtype, drop, seed, sample=None):
     (32, 2, 512, "bf16", 0.0),      # decode-sized: weight-streaming kernel
     (48, 4, 264, "bf16", 0.2),      # ragged d, dropped slots
     (1, 1, 128, "bf16", 0.0),       # one token, one slot
+    (16, 4, 2048, "bf16", 0.0),     # reduction 8192 split into two parts
+    (20, 4, 2104, "bf16", 0.1),     # reduction 8416 in two parts, the last one ragged
+    (50, 2, 4096, "bf16", 0.1),     # 33..64 rows: four token blocks per pass, split reduction
     (300, 2, 256, "bf16", 0.1),     # tiled GEMM, ragged rows
     (1000, 2, 384, "bf16", 0.0),    # tiled GEMM, several row tiles
     (700, 3, 200, "bf16", 0.3),     # reduction length K*d not a multiple of 64
