@@ -90,7 +90,9 @@ def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use
     a HIP graph and replayed (the library's launches are capture-safe: no
     allocation, no memset, no host synchronisation).  The dominant kernel's
     launch time is then measured over `steps` eager passes with HIP events
-    recorded on the kernel's own stream (outside the timed region)."""
+    recorded on the kernel's own stream (outside the timed region); the same
+    eager passes give the spread of the per-pass device time (HIP events
+    around each layer call: p10, median, p90)."""
     import torch
     import mixture_experts_layer_38_amd as moe
     y = torch.empty((cfg.T, cfg.d), dtype=layer.torch_dtype, device="cuda")
@@ -127,15 +129,22 @@ def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use
     for e in starts + stops:  # materialise the underlying hipEvent_t
         e.record()
     torch.cuda.synchronize()
+    step_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    step_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     keep = moe.moe_set_kernel_timer(kernel, starts, stops)
-    for _ in range(steps):
+    for i in range(steps):
+        step_a[i].record()
         layer.forward(x, bias, y=y)
+        step_b[i].record()
     torch.cuda.synchronize()
     n_rec = moe.moe_kernel_timer_count(kernel)
     moe.moe_set_kernel_timer(kernel, [], [])
     del keep
     kern_ms = [starts[i].elapsed_time(stops[i]) for i in range(n_rec)]
-    return wall, float(np.mean(kern_ms)) if kern_ms else float("nan"), counts, kept
+    step_ms = np.array([step_a[i].elapsed_time(step_b[i]) for i in range(steps)])
+    spread = {"p10": float(np.percentile(step_ms, 10)), "median": float(np.median(step_ms)),
+              "p90": float(np.percentile(step_ms, 90)), "passes": int(steps)}
+    return wall, float(np.mean(kern_ms)) if kern_ms else float("nan"), counts, kept, spread
 
 
 def time_chunked(cfg, layer, x, bias, chunk: int, steps: int):
@@ -280,14 +289,24 @@ def main():
     x = to_device(inp["x"], cfg.dtype)
     bias = None if inp["logit_bias"] is None else torch.from_numpy(inp["logit_bias"]).cuda()
     print("[bench] timing", file=sys.stderr, flush=True)
-    wall, k_ms, counts, kept = time_workload(cfg, layer, x, bias, args.steps, args.warmup, "ffn_gate_up",
-                                              args.graph)
+    wall, k_ms, counts, kept, spread = time_workload(cfg, layer, x, bias, args.steps, args.warmup, "ffn_gate_up",
+                                                      args.graph)
     ms_step = wall / args.steps * 1e3
     tok_s = cfg.T * args.steps / wall
     gb, gf = gate_up_algorithmic(cfg, kept)
     lb, lf = layer_algorithmic(cfg, kept)
-    achieved = gb / (k_ms * 1e-3) / 1e9
     traffic = load_traffic(cfg.name, "ffn_gate_up", "decode" if cfg.T <= 64 else "prefill")
+    # the gate/up launch is bounded by the MFMA peak when its arithmetic
+    # intensity is above the ridge point of the two peaks, else by HBM
+    if gf / gb > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "kernel": "ffn_gate_up", "achieved": gf / (k_ms * 1e-3) / 1e12,
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
+        roof.update(frac=roof["achieved"] / MFMA_BF16_PEAK_TFS, traffic=traffic, kernel_ms=k_ms,
+                    algorithmic_flops=gf)
+    else:
+        roof = {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": gb / (k_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof.update(frac=roof["achieved"] / HBM_PEAK_GBS, traffic=traffic, kernel_ms=k_ms, algorithmic_bytes=gb)
     result = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
@@ -296,9 +315,8 @@ def main():
                                f"F={cfg.F} {cfg.dtype}", "T": cfg.T, "d_model": cfg.d,
                    "experts": cfg.E, "top_k": cfg.K, "d_ff": cfg.F, "capacity": cfg.capacity,
                    "launch": "hip graph replay" if args.graph else "eager"},
-        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel_ms": k_ms, "algorithmic_bytes": gb},
+        "roofline": roof,
+        "step_ms": spread,
         "layer": {"hbm_frac": lb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "algorithmic_bytes": lb, "algorithmic_flops": lf,
                   "counts": counts.tolist()},
@@ -314,8 +332,8 @@ def main():
         px = to_device(pin["x"], pcfg.dtype)
         pb = torch.from_numpy(pin["logit_bias"]).cuda()
         print("[bench] timing prefill", file=sys.stderr, flush=True)
-        pwall, pk_ms, pcounts, pkept = time_workload(pcfg, player, px, pb, args.prefill_steps, 2,
-                                                     "ffn_gate_up", args.graph)
+        pwall, pk_ms, pcounts, pkept, pspread = time_workload(pcfg, player, px, pb, args.prefill_steps, 2,
+                                                              "ffn_gate_up", args.graph)
         pgb, pgf = gate_up_algorithmic(pcfg, pkept)
         plb, plf = layer_algorithmic(pcfg, pkept)
         pms = pwall / args.prefill_steps * 1e3
@@ -327,6 +345,7 @@ def main():
                          "achieved": pgf / (pk_ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": pgf / (pk_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
                          "traffic": load_traffic(pcfg.name, "ffn_gate_up", "prefill"), "kernel_ms": pk_ms},
+            "step_ms": pspread,
             "layer_mfma_frac": plf / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
             "counts": pcounts.tolist(),
             "chunked": time_chunked(pcfg, player, px, pb, args.prefill_chunk, args.prefill_steps),
