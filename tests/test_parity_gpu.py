@@ -34,6 +34,12 @@ REDUCED = {
     # decode-sized batches that take the one-launch router + dispatch path
     "small_e16_ragged_d": scaled(C["dsv3_routed"], T=37, d=584, E=16, K=4, F=256),
     "small_t64_e16": scaled(C["capacity_top2"], T=64, d=256, E=16, F=128),
+    # the largest sizes the boundary accepts: E = 1024 with K = 32 (one-stage
+    # reductions, every expert on the weight-streaming kernel), d = 65536 on
+    # the decode path, F = 65536 on the prefill path
+    "max_e1024_k32": scaled(C["dsv3_routed"], T=96, d=64, E=1024, K=32, F=64),
+    "max_d65536_decode": scaled(C["mixtral_decode"], T=40, d=65536, E=2, K=1, F=64),
+    "max_f65536_prefill": scaled(C["mixtral_prefill"], T=100, d=128, E=2, K=2, F=65536),
 }
 
 

@@ -33,7 +33,7 @@ def _empty(shape, dtype):
 @pytest.mark.parametrize("E,K,with_bias,flags", [(8, 2, False, 0), (8, 1, True, 0), (64, 2, True, 0),
                                                   (256, 8, True, 0), (5, 5, False, 0), (1000, 7, True, 0),
                                                   (64, 2, True, 1), (256, 8, True, 1), (1000, 7, True, 3),
-                                                  (8, 2, True, 2)])
+                                                  (8, 2, True, 2), (1024, 32, True, 0), (1024, 32, False, 3)])
 def test_route_given_logits_with_ties(orc, E, K, with_bias, flags):
     """x = NULL mode: the GPU routes logits chosen by the test, full of exact
     ties and signed zeros; ids must match the oracle bit for bit."""
@@ -64,7 +64,8 @@ def test_route_given_logits_with_ties(orc, E, K, with_bias, flags):
 
 @pytest.mark.parametrize("T,E,K,cap", [(1, 8, 2, -1), (5, 1, 1, -1), (1000, 8, 2, -1), (1000, 8, 2, 100),
                                        (5000, 64, 2, 7), (4096, 256, 8, -1), (3000, 1024, 4, 3),
-                                       (777, 16, 4, 0), (2500, 3, 2, 1)])
+                                       (777, 16, 4, 0), (2500, 3, 2, 1), (2000, 1024, 32, -1),
+                                       (1500, 512, 32, 20)])
 def test_dispatch_oracle_ids(orc, T, E, K, cap):
     """Dispatch of skewed ids picked by the test: counts, kept, offsets and both
     row maps bit-exact; gathered rows are exact copies of x."""
