@@ -18,6 +18,9 @@ pytestmark = pytest.mark.gpu
     ("decode", scaled(CONFIGS["mixtral_decode"], d=512, F=1536)),
     ("prefill", scaled(CONFIGS["mixtral_prefill"], T=1500, d=512, F=1024)),
     ("capacity", scaled(CONFIGS["capacity_top2"], T=2048, d=256, F=1408)),
+    # 256 experts of about 16 rows: the tile plan sends them to the
+    # weight-streaming kernel, a choice made on the device at every replay
+    ("dsv3", scaled(CONFIGS["dsv3_routed"], T=512, d=256, F=256)),
 ])
 def test_graph_replay_matches_eager(name, cfg):
     import torch
