@@ -6,6 +6,8 @@
 //  aux:     same notes §1.2, aux = E * sum_e f_e P_e.
 //  bias:    engineering page (ybb.press/quantum-computing/18594) §1.2, one
 //           +-alpha step toward the average load T*K/E.
+#include <algorithm>
+
 #include "../device_common.h"
 #include "../launch.h"
 
@@ -88,6 +90,7 @@ size_t combine_concat_ws_bytes(int T, int K, int d, int dtype) {
     const size_t es = dtype == MOE_DTYPE_F32 ? 4 : 2;
     size_t b = align_up((size_t)T * K * d * es, 256) + 256;
     if (dtype == MOE_DTYPE_BF16) b += linear_ws_bytes(T, d, K * d);
+    if (dtype == MOE_DTYPE_BF16 && concat_small_ok(T, K, d)) b = std::max(b, concat_small_ws_bytes(T, K, d));
     return b;
 }
 
@@ -109,6 +112,7 @@ hipError_t launch_combine_concat(int T, int K, int d, int dtype, const void* h, 
                                                                        (const float*)w_cat, (float*)y);
         return hipGetLastError();
     }
+    if (concat_small_ok(T, K, d)) return launch_concat_small(T, K, d, h, assign_row, w_cat, y, ws, s);
     concat_gather_kernel<bf16><<<grid, 256, 0, s>>>(T, K, d, (const bf16*)h, assign_row, (bf16*)x, offs);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

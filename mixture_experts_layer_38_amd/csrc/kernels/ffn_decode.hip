@@ -39,21 +39,25 @@ __device__ __forceinline__ u32x4 load16_masked(const bf16* row, int k, int K) {
 }
 
 // The rows of expert e against this workgroup's strip of weight rows.
-// K is the reduction length and ldk the row stride of A and of the weights
-// (ldk > K when the caller splits the reduction).  PART writes the fp32 sums
-// to part [n_rows, N] instead of bf16 to out.
-template <bool GATED, int CPI, int NCB, bool ALIGNED, int R, bool PART = false>
+// K is the reduction length; lda and ldw are the row strides of A and of the
+// weights (larger than K when the caller splits the reduction).  offsets may
+// be NULL: then the group is rows [0, n_rows).  PART writes the fp32 sums to
+// part [n_rows, N] instead of bf16 to out.  ZNEG reads row r of the group
+// from A row rowmap[r * topk] as is, or as zeros when that entry is negative
+// (the slots of a concatenation); otherwise row r is A row
+// rowmap[r] / topk (rowmap NULL: row r).
+template <bool GATED, int CPI, int NCB, bool ALIGNED, int R, bool PART = false, bool ZNEG = false>
 __device__ __forceinline__ void ffn_decode_group(
     int e, int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
     const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
-    bf16* __restrict__ out, int ldk, float* __restrict__ part = nullptr) {
+    bf16* __restrict__ out, int lda, int ldw, float* __restrict__ part = nullptr) {
     constexpr int NG = GATED ? 2 : 1;
     constexpr int NS = 4 * CPI;          // 32-wide slices per chunk
     constexpr int KCH = DC_KCH * CPI;  // k per chunk
     __shared__ float red[DC_WAVES - 1][R][NCB][NG][4][kWave];
     const int n0 = blockIdx.x * DC_ROWS * R;
-    const int r0 = offsets[e];
-    const int m = min(offsets[e + 1], n_rows) - r0;
+    const int r0 = offsets ? offsets[e] : 0;
+    const int m = (offsets ? min(offsets[e + 1], n_rows) : n_rows) - r0;
     if (r0 < 0 || m <= 0) return;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -69,8 +73,8 @@ __device__ __forceinline__ void ffn_decode_group(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int wrow = min(n0 + DC_ROWS * r + rl, N - 1);
-        wa[r] = Wa + ((size_t)e * N + wrow) * ldk;
-        wb[r] = GATED ? Wb + ((size_t)e * N + wrow) * ldk : nullptr;
+        wa[r] = Wa + ((size_t)e * N + wrow) * ldw;
+        wb[r] = GATED ? Wb + ((size_t)e * N + wrow) * ldw : nullptr;
     }
     const int kl = g * 8;  // this lane's k offset inside each 32-wide slice
 
@@ -85,9 +89,21 @@ __device__ __forceinline__ void ffn_decode_group(
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) acc[r][cb][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
         const bf16* arow[NCB];
+        bool azero[NCB];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-            arow[cb] = A + (size_t)src_row(rowmap, topk, r0 + p0 + min(cb * 16 + rl, mp - 1)) * ldk;
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int r = r0 + p0 + min(cb * 16 + rl, mp - 1);
+            if (ZNEG) {
+                // a dropped slot never touches A: its (discarded) loads read
+                // the first weight row of the strip, which spans the same k
+                const int a = rowmap[(size_t)r * topk];
+                azero[cb] = a < 0;
+                arow[cb] = a < 0 ? wa[0] : A + (size_t)a * lda;
+            } else {
+                azero[cb] = false;
+                arow[cb] = A + (size_t)src_row(rowmap, topk, r) * lda;
+            }
+        }
 
         // Double buffer in registers: the weight loads of chunk c + 1 are issued
         // after the token loads of chunk c, so waiting for the tokens of chunk c
@@ -119,6 +135,7 @@ __device__ __forceinline__ void ffn_decode_group(
                     for (int s = 0; s < NS; ++s) {
                         const int k = c * KCH + s * 32 + kl;
                         xv[cb][s] = ALIGNED ? load16(arow[cb] + k) : load16_masked(arow[cb], k, K);
+                        if (ZNEG) xv[cb][s] = azero[cb] ? u32x4{0u, 0u, 0u, 0u} : xv[cb][s];
                     }
                 }
             }
@@ -207,7 +224,7 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
     const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
     bf16* __restrict__ out) {
     ffn_decode_group<GATED, CPI, NCB, ALIGNED, R>(blockIdx.y, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out,
-                                                  K);
+                                                  K, K);
 }
 
 // The experts listed in elist[0 .. *ecount) (small groups of a large batch),
@@ -220,7 +237,7 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_small_experts_kernel(
     const int cnt = *ecount;
     for (int i = blockIdx.y; i < cnt; i += gridDim.y)
         ffn_decode_group<GATED, CPI, NCB, ALIGNED, R>(elist[i], n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb,
-                                                      out, K);
+                                                      out, K, K);
 }
 
 template <bool ALIGNED>
@@ -290,8 +307,24 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void linear_part_kernel(
     const bf16* __restrict__ W, float* __restrict__ part) {
     const int kb = blockIdx.y * kp;
     ffn_decode_group<false, 1, NCB, ALIGNED, 2, true>(0, n_rows, N, min(kp, K - kb), A + kb, nullptr, 1, offs,
-                                                      W + kb, nullptr, nullptr, K,
+                                                      W + kb, nullptr, nullptr, K, K,
                                                       part + (size_t)blockIdx.y * n_rows * N);
+}
+
+// Concatenation combine for at most 64 tokens (MoE notes §2.3): part p of
+// the reduction over W_cat [d, Ks d] covers columns [c0, c0 + kp) of slot
+// j = p / qs (c0 = (p % qs) kp), so its token rows are the grouped expert
+// rows h[assign_row[t Ks + j]] read in place (a dropped slot reads as zeros)
+// and no concatenated copy is built.
+template <bool ALIGNED, int NCB>
+__global__ __launch_bounds__(DC_WAVES * kWave) void concat_part_kernel(
+    int T, int d, int Ks, int kp, int qs, const bf16* __restrict__ h, const int32_t* __restrict__ assign_row,
+    const bf16* __restrict__ W, float* __restrict__ part) {
+    const int j = blockIdx.y / qs;
+    const int c0 = (blockIdx.y - j * qs) * kp;
+    ffn_decode_group<false, 1, NCB, ALIGNED, 2, true, true>(0, T, d, min(kp, d - c0), h + c0, assign_row + j, Ks,
+                                                            nullptr, W + (size_t)j * d + c0, nullptr, nullptr, d,
+                                                            Ks * d, part + (size_t)blockIdx.y * T * d);
 }
 
 __global__ __launch_bounds__(256) void linear_part_reduce_kernel(int n, int parts, const float* __restrict__ part,
@@ -356,6 +389,58 @@ hipError_t launch_linear_small(int n_rows, int N, int K, const void* A, const in
     else
         ffn_decode_kernel<false, 1, 4, false, 2><<<g, DC_WAVES * kWave, 0, s>>>(
             n_rows, N, K, (const bf16*)A, nullptr, 1, offs, (const bf16*)w, nullptr, (bf16*)out);
+    return hipGetLastError();
+}
+
+// Parts per slot for the concatenation combine: the count the plain linear
+// layer would use, spread over the Ks slots (at least one per slot); 0 when
+// the concatenation is not decode-sized or would need more than
+// LIN_MAX_PARTS parts (the caller then gathers the rows and uses
+// launch_linear).
+static int concat_parts_per_slot(int T, int Ks, int d, int* kp) {
+    if (T > LIN_SMALL_ROWS || d % 4 != 0) return 0;
+    int kpl;
+    const int parts = linear_parts(d, Ks * d, &kpl);
+    const int q = std::max(1, parts / Ks);
+    if (Ks * q > LIN_MAX_PARTS) return 0;
+    *kp = ((d + q - 1) / q + DC_KCH - 1) / DC_KCH * DC_KCH;
+    return (d + *kp - 1) / *kp;
+}
+
+size_t concat_small_ws_bytes(int T, int Ks, int d) {
+    int kp;
+    const int qs = concat_parts_per_slot(T, Ks, d, &kp);
+    return qs ? (size_t)Ks * qs * T * d * sizeof(float) : 0;
+}
+
+bool concat_small_ok(int T, int Ks, int d) {
+    int kp;
+    return concat_parts_per_slot(T, Ks, d, &kp) > 0;
+}
+
+hipError_t launch_concat_small(int T, int Ks, int d, const void* h, const int32_t* assign_row, const void* w_cat,
+                               void* y, void* ws, hipStream_t s) {
+    int kp;
+    const int qs = concat_parts_per_slot(T, Ks, d, &kp);
+    if (qs == 0) return hipErrorInvalidValue;
+    const int parts = Ks * qs;
+    dim3 g((d + 2 * DC_ROWS - 1) / (2 * DC_ROWS), parts);
+    float* part = reinterpret_cast<float*>(ws);
+    const bf16* hb = (const bf16*)h;
+    const bf16* wt = (const bf16*)w_cat;
+    const bool al = d % kp == 0 && kp % DC_KCH == 0;
+    if (T <= 32) {
+        if (al) concat_part_kernel<true, 2><<<g, DC_WAVES * kWave, 0, s>>>(T, d, Ks, kp, qs, hb, assign_row, wt, part);
+        else concat_part_kernel<false, 2><<<g, DC_WAVES * kWave, 0, s>>>(T, d, Ks, kp, qs, hb, assign_row, wt, part);
+    } else {
+        if (al) concat_part_kernel<true, 4><<<g, DC_WAVES * kWave, 0, s>>>(T, d, Ks, kp, qs, hb, assign_row, wt, part);
+        else concat_part_kernel<false, 4><<<g, DC_WAVES * kWave, 0, s>>>(T, d, Ks, kp, qs, hb, assign_row, wt, part);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int n = T * d;
+    linear_part_reduce_kernel<<<std::max(1, std::min((n + 255) / 256, 1024)), 256, 0, s>>>(n, parts, part,
+                                                                                          (bf16*)y);
     return hipGetLastError();
 }
 

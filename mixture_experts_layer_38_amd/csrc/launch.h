@@ -88,6 +88,14 @@ hipError_t launch_linear_small(int n_rows, int N, int K, const void* A, const in
                                void* out, void* ws, hipStream_t s);
 hipError_t launch_linear(int n_rows, int N, int K, const void* x, const int32_t* offs, const void* w,
                          void* y, void* ws, hipStream_t s);
+// Concatenation combine for at most LIN_SMALL_ROWS tokens (bf16): the
+// weight-streaming kernel reads each slot's grouped rows h[assign_row[t,k]]
+// in place, its reduction split into parts that never straddle a slot.
+// concat_small_ok says whether this path applies; ws: concat_small_ws_bytes.
+bool concat_small_ok(int T, int Ks, int d);
+size_t concat_small_ws_bytes(int T, int Ks, int d);
+hipError_t launch_concat_small(int T, int Ks, int d, const void* h, const int32_t* assign_row, const void* w_cat,
+                               void* y, void* ws, hipStream_t s);
 // ---- combine / aux / bias --------------------------------------------------
 // Concatenation combine: y[t] = W_cat . concat over slots of h[assign_row[t,k]].
 size_t combine_concat_ws_bytes(int T, int K, int d, int dtype);

@@ -2,11 +2,11 @@
 
 MoE notes §2.3: the K expert outputs of a token are concatenated in slot
 order (a slot dropped by capacity is a block of zeros) and passed through one
-linear layer W_cat [d, K*d].  Reduced cases compare every element; the
-Mixtral-sized cases (the decode batch through the weight-streaming kernel
-with its reduction split into parts,
-the prefill batch through the tiled GEMM with its last-round split) compare
-sampled tokens.
+linear layer W_cat [d, K*d].  Up to 64 tokens take the weight-streaming
+kernel, which reads each slot's rows of h in place with its reduction split
+into parts; more tokens gather the concatenation and take the tiled GEMM.
+Reduced cases compare every element; the Mixtral-sized cases (the decode and
+the prefill batch) compare sampled tokens.
 """
 from __future__ import annotations
 
@@ -76,6 +76,8 @@ def _run(orc, T, K, d, dtype, drop, seed, sample=None):
     (16, 4, 2048, "bf16", 0.0),     # reduction 8192 split into two parts
     (20, 4, 2104, "bf16", 0.1),     # reduction 8416 in two parts, the last one ragged
     (50, 2, 4096, "bf16", 0.1),     # 33..64 rows: four token blocks per pass, split reduction
+    (24, 1, 8192, "bf16", 0.3),     # one slot split into two parts, dropped rows in both
+    (24, 1, 8200, "bf16", 0.2),     # one slot in two parts, the last one ragged
     (300, 2, 256, "bf16", 0.1),     # tiled GEMM, ragged rows
     (1000, 2, 384, "bf16", 0.0),    # tiled GEMM, several row tiles
     (700, 3, 200, "bf16", 0.3),     # reduction length K*d not a multiple of 64
@@ -86,8 +88,9 @@ def test_combine_concat_reduced(orc, T, K, d, dtype, drop):
     _run(orc, T, K, d, dtype, drop, seed=T * 31 + K)
 
 
-def test_combine_concat_all_dropped(orc):
-    _run(orc, 100, 2, 128, "bf16", 1.0, seed=5)
+@pytest.mark.parametrize("T", [30, 100])
+def test_combine_concat_all_dropped(orc, T):
+    _run(orc, T, 2, 128, "bf16", 1.0, seed=5)
 
 
 @pytest.mark.parametrize("T", [32, 8192])
