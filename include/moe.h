@@ -68,7 +68,9 @@ enum { MOE_FLAG_BIAS_SELECT_ONLY = 1u, MOE_FLAG_COMBINE_MEAN = 2u };
  *   n_experts E, 1 <= E <= 1024
  *   top_k     K, 1 <= K <= min(E, 32)
  *   d_ff      F, multiple of 8, <= 65536
- *   dtype     moe_dtype of activations and expert / router weights
+ *   dtype     moe_dtype of activations and expert / router weights; fp32
+ *             (the small-layer path) also needs T*K*max(d, F) <= 2^31 and
+ *             T*E <= 2^31
  *   capacity  < 0: unlimited; >= 0: at most `capacity` rows kept per expert,
  *             in flat assignment order t*K + k ([NOTES] §3.1: a capacity
  *             factor cf gives capacity = floor(cf * T * K / E), computed by the

@@ -2,7 +2,7 @@
 //  - bf16 with at most 64 tokens (so at most 64 rows per expert): the
 //    weight-streaming decode kernels (ffn_decode.hip);
 //  - other bf16 problems: the LDS-tiled MFMA kernels (ffn_prefill.hip);
-//  - fp32: plain FMA kernels below (one thread per output element), kept for
+//  - fp32: plain FMA kernels below (one wave per output element), kept for
 //    the small fp32 layer.
 #include "../device_common.h"
 #include "../launch.h"
@@ -30,6 +30,9 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int 
     return lo;
 }
 
+// fp32 kernels: one wave per output element.  Lane l takes k = l, l + 64, ...
+// (so each load instruction reads 256 contiguous bytes of the weight row and
+// of the token row), then the 64 partial sums meet in a fixed-order butterfly.
 __global__ __launch_bounds__(256) void ffn_f32_gate_up_kernel(int n_rows, int E, int F, int d,
                                                              const float* __restrict__ A,
                                                              const int32_t* __restrict__ rowmap, int topk,
@@ -37,7 +40,8 @@ __global__ __launch_bounds__(256) void ffn_f32_gate_up_kernel(int n_rows, int E,
                                                              const float* __restrict__ w1,
                                                              const float* __restrict__ w3,
                                                              float* __restrict__ act) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) / kWave;  // output of this wave
+    const int lane = lane_id();
     const int S = min(offsets[E], n_rows);
     if (i >= (size_t)S * F) return;
     const int row = (int)(i / F);
@@ -47,11 +51,14 @@ __global__ __launch_bounds__(256) void ffn_f32_gate_up_kernel(int n_rows, int E,
     const float* r1 = w1 + ((size_t)e * F + f) * d;
     const float* r3 = w3 + ((size_t)e * F + f) * d;
     float g1 = 0.0f, g3 = 0.0f;
-    for (int j = 0; j < d; ++j) {
-        g1 = fmaf(r1[j], a[j], g1);
-        g3 = fmaf(r3[j], a[j], g3);
+    for (int j = lane; j < d; j += kWave) {
+        const float av = a[j];
+        g1 = fmaf(r1[j], av, g1);
+        g3 = fmaf(r3[j], av, g3);
     }
-    act[i] = g1 / (1.0f + expf(-g1)) * g3;
+    g1 = wave_sum(g1);
+    g3 = wave_sum(g3);
+    if (lane == 0) act[i] = g1 / (1.0f + expf(-g1)) * g3;
 }
 
 __global__ __launch_bounds__(256) void ffn_f32_down_kernel(int n_rows, int E, int F, int d,
@@ -59,7 +66,8 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(int n_rows, int E, in
                                                           const int32_t* __restrict__ offsets,
                                                           const float* __restrict__ w2,
                                                           float* __restrict__ h) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) / kWave;
+    const int lane = lane_id();
     const int S = min(offsets[E], n_rows);
     if (i >= (size_t)S * d) return;
     const int row = (int)(i / d);
@@ -67,9 +75,10 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(int n_rows, int E, in
     const int e = expert_of_row(offsets, E, row);
     const float* a = act + (size_t)row * F;
     const float* r2 = w2 + ((size_t)e * d + c) * F;
-    float s = 0.0f;
-    for (int f = 0; f < F; ++f) s = fmaf(r2[f], a[f], s);
-    h[i] = s;
+    float sum = 0.0f;
+    for (int f = lane; f < F; f += kWave) sum = fmaf(r2[f], a[f], sum);
+    sum = wave_sum(sum);
+    if (lane == 0) h[i] = sum;
 }
 
 static bool use_decode(int T, int dtype) { return dtype == MOE_DTYPE_BF16 && T <= kDecodeMaxTokens; }
@@ -85,14 +94,15 @@ hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* 
     const int n = T * K;
     if (dtype == MOE_DTYPE_F32) {
         const size_t n1 = (size_t)n * F, n2 = (size_t)n * d;
+        // one wave (a quarter of a 256-thread block) per output element
         MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_GATE_UP, s,
-                         ffn_f32_gate_up_kernel<<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
+                         ffn_f32_gate_up_kernel<<<(unsigned)((n1 + 3) / 4), 256, 0, s>>>(
                              n, E, F, d, (const float*)A, rowmap, K, offsets, (const float*)w1,
                              (const float*)w3, (float*)act));
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
-                         ffn_f32_down_kernel<<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
+                         ffn_f32_down_kernel<<<(unsigned)((n2 + 3) / 4), 256, 0, s>>>(
                              n, E, F, d, (const float*)act, offsets, (const float*)w2, (float*)h));
         return hipGetLastError();
     }

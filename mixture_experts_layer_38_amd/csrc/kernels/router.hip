@@ -340,18 +340,22 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, i
 }
 
 // fp32 scores: one thread per (token, expert), plain FMA over d.
+// fp32 scores: one wave per (token, expert); lane l takes j = l, l + 64, ...
+// of the token row, then a fixed-order wave sum.
 __global__ __launch_bounds__(256) void router_logits_f32_kernel(int T, int d, int E,
                                                                const float* __restrict__ x,
                                                                const float* __restrict__ wr,
                                                                float* __restrict__ logits) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) / kWave;
+    const int lane = lane_id();
     if (i >= (size_t)T * E) return;
     const int t = (int)(i / E);
     const int e = (int)(i - (size_t)t * E);
     const float* xr = x + (size_t)t * d;
     float s = 0.0f;
-    for (int j = 0; j < d; ++j) s = fmaf(xr[j], wr[(size_t)j * E + e], s);
-    logits[i] = s;
+    for (int j = lane; j < d; j += kWave) s = fmaf(xr[j], wr[(size_t)j * E + e], s);
+    s = wave_sum(s);
+    if (lane == 0) logits[i] = s;
 }
 
 // ---- small batches: two launches for the whole front of the layer -----------
@@ -613,7 +617,7 @@ hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const
         }
     } else if (x != nullptr) {  // fp32 scores
         const size_t n = (size_t)T * E;
-        router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+        router_logits_f32_kernel<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(
             T, d, E, (const float*)x, (const float*)w_router, logits);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }

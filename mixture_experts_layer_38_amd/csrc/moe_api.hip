@@ -46,6 +46,11 @@ static moe_status check_problem(const moe_problem* p) {
     if (p->d_model % 8 != 0 || p->d_ff % 8 != 0) return MOE_ERR_UNSUPPORTED;
     if (p->d_model > 65536 || p->d_ff > 65536) return MOE_ERR_UNSUPPORTED;
     if ((int64_t)p->T * p->top_k >= (1LL << 30)) return MOE_ERR_UNSUPPORTED;
+    // the fp32 kernels run one wave per output element: keep their grids in range
+    if (p->dtype == MOE_DTYPE_F32 &&
+        ((int64_t)p->T * p->top_k * std::max(p->d_model, p->d_ff) > (1LL << 31) ||
+         (int64_t)p->T * p->n_experts > (1LL << 31)))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 

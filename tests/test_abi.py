@@ -51,6 +51,8 @@ def _ws(p):
     (dict(d_ff=1410), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED), (dict(flags=4), INVALID),
     (dict(flags=3), OK),
     (dict(n_experts=64, top_k=33), UNSUPPORTED), (dict(T=1 << 29, top_k=2), UNSUPPORTED),
+    (dict(dtype=0, T=1 << 20, top_k=2, d_model=2048), UNSUPPORTED),
+    (dict(dtype=0, T=1 << 20, top_k=2, d_model=1024), OK),
 ])
 def test_problem_checks(kw, status):
     base = dict(T=64, d_model=128, n_experts=8, top_k=2, d_ff=256, dtype=1, capacity=-1, flags=0)
