@@ -268,7 +268,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip the routing/combine variants and router losses")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per pass instead of launching eagerly "
-                         "(measured about 1% slower on the decode step)")
+                         "(measured about 1%% slower on the decode step)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path "

@@ -43,7 +43,10 @@ __device__ __forceinline__ int src_row(const int32_t* rowmap, int topk, int r) {
     return a < 0 ? 0 : a / topk;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z * sigmoid(z), with the hardware reciprocal (1 ulp) in place of
+// an IEEE divide: the result is rounded to bf16 or summed in fp32 next.
+// exp(-z) = inf for very negative z gives z * 0 = -0, the limit.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {
