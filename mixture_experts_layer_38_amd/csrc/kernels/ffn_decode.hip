@@ -252,11 +252,13 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A
                          (bf16*)act));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // Two 16-row blocks per workgroup for the down projection: each token
-    // fragment (an L2 read of the long activation rows) feeds two MFMAs.
-    dim3 g2((d + 2 * DC_ROWS - 1) / (2 * DC_ROWS), E);
+    // Four 16-row blocks per workgroup for the down projection: each token
+    // fragment (an L2 read of the long activation rows) feeds four MFMAs.
+    // Measured on the Mixtral-shaped decode batch: one block 26 us slower per
+    // layer than two, four 1.7 us faster than two.
+    dim3 g2((d + 4 * DC_ROWS - 1) / (4 * DC_ROWS), E);
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
-                     ffn_decode_kernel<false, 1, 1, ALIGNED, 2><<<g2, DC_WAVES * kWave, 0, s>>>(
+                     ffn_decode_kernel<false, 1, 1, ALIGNED, 4><<<g2, DC_WAVES * kWave, 0, s>>>(
                          n_rows, d, F, (const bf16*)act, nullptr, 1, offsets, (const bf16*)w2, nullptr, (bf16*)h));
     return hipGetLastError();
 }
