@@ -246,7 +246,7 @@ void ffn_prefill_kernel(
             b_src[j] = Wa + ((size_t)e * N + nr) * K + (size_t)ks0 * PF_BK + c * 8;
         }
     }
-    auto issue_a = [&](int kt, bf16* dA) {
+    auto issue_a = [&](int kt, bf16* dA) __attribute__((always_inline)) {
         const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
         for (int j = 0; j < NJA; ++j)
@@ -254,7 +254,7 @@ void ffn_prefill_kernel(
                                              (__attribute__((address_space(3))) void*)(dA + 8 * (wave + 4 * j) * PF_BK),
                                              16, 0, 0);
     };
-    auto issue_b = [&](int kt, bf16* dB) {
+    auto issue_b = [&](int kt, bf16* dB) __attribute__((always_inline)) {
         const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
         for (int j = 0; j < NJB; ++j)
@@ -262,7 +262,7 @@ void ffn_prefill_kernel(
                                              (__attribute__((address_space(3))) void*)(dB + 8 * (wave + 4 * j) * PF_BK),
                                              16, 0, 0);
     };
-    auto issue = [&](int kt, bf16* dA, bf16* dB) {
+    auto issue = [&](int kt, bf16* dA, bf16* dB) __attribute__((always_inline)) {
         issue_a(kt, dA);
         issue_b(kt, dB);
     };
@@ -288,45 +288,49 @@ void ffn_prefill_kernel(
     struct Frags {
         bf16x8 w[4], t[NTB];
     };
-    // 16-wide k quarter q of a stage: chunk 2q + (lane / 32).
-    auto read = [&](const bf16* cA, const bf16* cB, int q, Frags& f) {
+    // 16-wide k quarter q of a stage: chunk 2q + (lane / 32).  nb: the
+    // token blocks this wave multiplies (NTB, or fewer on a partly filled
+    // tile whose last blocks hold only padded rows).
+    auto read = [&](auto nb, const bf16* cA, const bf16* cB, int q, Frags& f) __attribute__((always_inline)) {
+        constexpr int NB = decltype(nb)::value;
         const int c = 2 * q + fhalf;
 #pragma unroll
         for (int wb = 0; wb < 4; ++wb)
             f.w[wb] = *reinterpret_cast<const bf16x8*>(
                 &cB[(wn * 128 + wb * 32 + (lane & 31)) * PF_BK + (c ^ wsw[wb]) * 8]);
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
+        for (int tb = 0; tb < NB; ++tb)
             f.t[tb] = *reinterpret_cast<const bf16x8*>(
                 &cA[(wm * (BM / 2) + tb * 32 + (lane & 31)) * PF_BK + (c ^ tsw[tb]) * 8]);
     };
-    auto mma = [&](const Frags& f) {
+    auto mma = [&](auto nb, const Frags& f) __attribute__((always_inline)) {
+        constexpr int NB = decltype(nb)::value;
 #pragma unroll
         for (int wb = 0; wb < 4; ++wb)
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) acc[wb][tb] = mfma32(f.w[wb], f.t[tb], acc[wb][tb]);
+            for (int tb = 0; tb < NB; ++tb) acc[wb][tb] = mfma32(f.w[wb], f.t[tb], acc[wb][tb]);
     };
     // Interleave: one MFMA, then one LDS fragment read, for every read of the
     // next quarter, then the remaining MFMAs (the reads issue in the shadow of
     // the MFMAs); NV loads (at most one per MFMA) are spread evenly over the
     // quarter's MFMAs.
-    auto interleave = [&](auto nv_c) {
+    auto interleave = [&](auto nb, auto nv_c) __attribute__((always_inline)) {
         constexpr int NV = decltype(nv_c)::value;
-        constexpr int NM = 4 * NTB;
-        static_assert(NV <= NM, "one load per MFMA at most");
+        constexpr int NM = 4 * decltype(nb)::value;
+        static_assert(NM == 0 || NV <= NM, "one load per MFMA at most");
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i < 4 + NTB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i < 4 + decltype(nb)::value) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             if (((i + 1) * NV) / NM > (i * NV) / NM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
     // After the barrier: the last quarter's MFMAs, NV loads and the reads of
     // the next stage's first quarter, one of each in turn, so no wave stalls
     // on a burst of loads with its MFMAs waiting.
-    auto interleave_loads = [&](auto nv_c) {
+    auto interleave_loads = [&](auto nb, auto nv_c) __attribute__((always_inline)) {
         constexpr int NV = decltype(nv_c)::value;
-        constexpr int NM = 4 * NTB, NR = 4 + NTB;
+        constexpr int NM = 4 * decltype(nb)::value, NR = 4 + decltype(nb)::value;
         constexpr int NI = NM > NV ? NM : NV;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -355,77 +359,77 @@ void ffn_prefill_kernel(
     // flight are the same on every path.
     Frags fa, fb;
     using IC0 = std::integral_constant<int, 0>;
-    auto step = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB) {
-        read(cA, cB, 1, fb);
-        mma(fa);
-        interleave(IC0{});
+    auto step = [&](auto nb, int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB) __attribute__((always_inline)) {
+        read(nb, cA, cB, 1, fb);
+        mma(nb, fa);
+        interleave(nb, IC0{});
         __builtin_amdgcn_sched_barrier(0);
-        read(cA, cB, 2, fa);
-        mma(fb);
-        interleave(IC0{});
+        read(nb, cA, cB, 2, fa);
+        mma(nb, fb);
+        interleave(nb, IC0{});
         __builtin_amdgcn_sched_barrier(0);
-        read(cA, cB, 3, fb);
-        mma(fa);
-        interleave(IC0{});
+        read(nb, cA, cB, 3, fb);
+        mma(nb, fa);
+        interleave(nb, IC0{});
         __builtin_amdgcn_sched_barrier(0);
         PF_WAIT_LGKM0();
         PF_WAIT_VM(NLD * (NSLOT - 2));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         issue(kt + NSLOT, cA, cB);
-        read(nA, nB, 0, fa);
-        mma(fb);
-        interleave_loads(std::integral_constant<int, NLD>{});
+        read(nb, nA, nB, 0, fa);
+        mma(nb, fb);
+        interleave_loads(nb, std::integral_constant<int, NLD>{});
         __builtin_amdgcn_sched_barrier(0);
     };
     // pA: the unit that receives A(kt + 2) during this step.
-    auto step5 = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB, bf16* pA) {
+    auto step5 = [&](auto nb, int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB, bf16* pA) __attribute__((always_inline)) {
         constexpr int V0 = (NJA + 2) / 3, V1 = (NJA + 1) / 3, V2 = NJA / 3;
         static_assert(V0 + V1 + V2 == NJA, "A loads per quarter");
         const size_t ko = (size_t)min(kt + 2, nk - 1) * PF_BK;
-        auto ld = [&](int j) {
+        auto ld = [&](int j) __attribute__((always_inline)) {
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[j] + ko),
                                              (__attribute__((address_space(3))) void*)(pA + 8 * (wave + 4 * j) * PF_BK),
                                              16, 0, 0);
         };
-        read(cA, cB, 1, fb);
+        read(nb, cA, cB, 1, fb);
 #pragma unroll
         for (int j = 0; j < V0; ++j) ld(j);
-        mma(fa);
-        interleave(std::integral_constant<int, V0>{});
+        mma(nb, fa);
+        interleave(nb, std::integral_constant<int, V0>{});
         __builtin_amdgcn_sched_barrier(0);
-        read(cA, cB, 2, fa);
+        read(nb, cA, cB, 2, fa);
 #pragma unroll
         for (int j = V0; j < V0 + V1; ++j) ld(j);
-        mma(fb);
-        interleave(std::integral_constant<int, V1>{});
+        mma(nb, fb);
+        interleave(nb, std::integral_constant<int, V1>{});
         __builtin_amdgcn_sched_barrier(0);
-        read(cA, cB, 3, fb);
+        read(nb, cA, cB, 3, fb);
 #pragma unroll
         for (int j = V0 + V1; j < NJA; ++j) ld(j);
-        mma(fa);
-        interleave(std::integral_constant<int, V2>{});
+        mma(nb, fa);
+        interleave(nb, std::integral_constant<int, V2>{});
         __builtin_amdgcn_sched_barrier(0);
         PF_WAIT_LGKM0();
         PF_WAIT_VM(NJA);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         issue_b(kt + 2, cA);
-        read(nA, nB, 0, fa);
-        mma(fb);
-        interleave_loads(std::integral_constant<int, NJB>{});
+        read(nb, nA, nB, 0, fa);
+        mma(nb, fb);
+        interleave_loads(nb, std::integral_constant<int, NJB>{});
         __builtin_amdgcn_sched_barrier(0);
     };
     // NSLOT 3: stage kt + 2 goes into slot (kt + 2) % 3, freed when stage
     // kt - 1 ended, with its loads spread over all four quarters of stage kt
     // (it is needed when stage kt + 1 ends); when stage kt ends only the
     // loads issued in its first three quarters may still be in flight.
-    auto step3 = [&](int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB, bf16* pA, bf16* pB) {
+    auto step3 = [&](auto nb, int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB, bf16* pA, bf16* pB) __attribute__((always_inline)) {
         constexpr int V = (NLD + 3) / 4;
         constexpr int V0 = V, V1 = V, V2 = V, V3 = NLD - 3 * V;
         static_assert(V3 >= 0, "loads per quarter");
         const size_t ko = (size_t)min(kt + 2, nk - 1) * PF_BK;
-        auto ld = [&](int i) {
+        auto ld = [&](int i) __attribute__((always_inline)) {
             if (i < NJA)
                 __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[i] + ko),
                                                  (__attribute__((address_space(3))) void*)(pA + 8 * (wave + 4 * i) * PF_BK),
@@ -435,23 +439,23 @@ void ffn_prefill_kernel(
                                                  (__attribute__((address_space(3))) void*)(pB + 8 * (wave + 4 * (i - NJA)) * PF_BK),
                                                  16, 0, 0);
         };
-        read(cA, cB, 1, fb);
+        read(nb, cA, cB, 1, fb);
 #pragma unroll
         for (int i = 0; i < V0; ++i) ld(i);
-        mma(fa);
-        interleave(std::integral_constant<int, V0>{});
+        mma(nb, fa);
+        interleave(nb, std::integral_constant<int, V0>{});
         __builtin_amdgcn_sched_barrier(0);
-        read(cA, cB, 2, fa);
+        read(nb, cA, cB, 2, fa);
 #pragma unroll
         for (int i = V0; i < V0 + V1; ++i) ld(i);
-        mma(fb);
-        interleave(std::integral_constant<int, V1>{});
+        mma(nb, fb);
+        interleave(nb, std::integral_constant<int, V1>{});
         __builtin_amdgcn_sched_barrier(0);
-        read(cA, cB, 3, fb);
+        read(nb, cA, cB, 3, fb);
 #pragma unroll
         for (int i = V0 + V1; i < V0 + V1 + V2; ++i) ld(i);
-        mma(fa);
-        interleave(std::integral_constant<int, V2>{});
+        mma(nb, fa);
+        interleave(nb, std::integral_constant<int, V2>{});
         __builtin_amdgcn_sched_barrier(0);
         PF_WAIT_LGKM0();
         PF_WAIT_VM(V0 + V1 + V2);
@@ -459,65 +463,91 @@ void ffn_prefill_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = V0 + V1 + V2; i < NLD; ++i) ld(i);
-        read(nA, nB, 0, fa);
-        mma(fb);
-        interleave_loads(std::integral_constant<int, V3>{});
+        read(nb, nA, nB, 0, fa);
+        mma(nb, fb);
+        interleave_loads(nb, std::integral_constant<int, V3>{});
         __builtin_amdgcn_sched_barrier(0);
     };
-    if (HALF) {
-        bf16* const u0 = sA0;
-        bf16* const u1 = sB0;
-        bf16* const u2 = sA1;
-        bf16* const u3 = sB1;
-        bf16* const u4 = sU4;
-        issue_a(0, u0);
-        issue_b(0, u1);
-        issue_a(1, u2);
-        issue_b(1, u3);
-        PF_WAIT_VM(NLD);
-        __builtin_amdgcn_s_barrier();
-        read(u0, u1, 0, fa);
-        const int nk_main = nk - nk % 5;
-        for (int k0 = 0; k0 < nk_main; k0 += 5) {
-            step5(k0, u0, u1, u2, u3, u4);
-            step5(k0 + 1, u2, u3, u4, u0, u1);
-            step5(k0 + 2, u4, u0, u1, u2, u3);
-            step5(k0 + 3, u1, u2, u3, u4, u0);
-            step5(k0 + 4, u3, u4, u0, u1, u2);
+    // The main loop for a wave that multiplies nb token blocks.  Every
+    // instance issues the same loads and barriers, so the waves of one
+    // workgroup may run different instances.
+    auto run = [&](auto nb) __attribute__((always_inline)) {
+        if (HALF) {
+            bf16* const u0 = sA0;
+            bf16* const u1 = sB0;
+            bf16* const u2 = sA1;
+            bf16* const u3 = sB1;
+            bf16* const u4 = sU4;
+            issue_a(0, u0);
+            issue_b(0, u1);
+            issue_a(1, u2);
+            issue_b(1, u3);
+            PF_WAIT_VM(NLD);
+            __builtin_amdgcn_s_barrier();
+            read(nb, u0, u1, 0, fa);
+            const int nk_main = nk - nk % 5;
+            for (int k0 = 0; k0 < nk_main; k0 += 5) {
+                step5(nb, k0, u0, u1, u2, u3, u4);
+                step5(nb, k0 + 1, u2, u3, u4, u0, u1);
+                step5(nb, k0 + 2, u4, u0, u1, u2, u3);
+                step5(nb, k0 + 3, u1, u2, u3, u4, u0);
+                step5(nb, k0 + 4, u3, u4, u0, u1, u2);
+            }
+            // The last nk % 5 stages start again at unit 0.
+            const int rem = nk - nk_main;
+            if (rem > 0) step5(nb, nk_main, u0, u1, u2, u3, u4);
+            if (rem > 1) step5(nb, nk_main + 1, u2, u3, u4, u0, u1);
+            if (rem > 2) step5(nb, nk_main + 2, u4, u0, u1, u2, u3);
+            if (rem > 3) step5(nb, nk_main + 3, u1, u2, u3, u4, u0);
+        } else if (NSLOT == 3) {
+            issue(0, sA0, sB0);
+            issue(1, sA1, sB1);
+            PF_WAIT_VM(NLD);
+            __builtin_amdgcn_s_barrier();
+            read(nb, sA0, sB0, 0, fa);
+            const int nk_main = nk - nk % 3;
+            for (int k0 = 0; k0 < nk_main; k0 += 3) {
+                step3(nb, k0, sA0, sB0, sA1, sB1, sA2, sB2);
+                step3(nb, k0 + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+                step3(nb, k0 + 2, sA2, sB2, sA0, sB0, sA1, sB1);
+            }
+            // The last nk % 3 stages start again at slot 0.
+            if (nk - nk_main > 0) step3(nb, nk_main, sA0, sB0, sA1, sB1, sA2, sB2);
+            if (nk - nk_main > 1) step3(nb, nk_main + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+        } else {
+            issue(0, sA0, sB0);
+            issue(1, sA1, sB1);
+            PF_WAIT_VM(NLD);
+            __builtin_amdgcn_s_barrier();
+            read(nb, sA0, sB0, 0, fa);
+            const int nk_main = nk - nk % 2;
+            for (int k0 = 0; k0 < nk_main; k0 += 2) {
+                step(nb, k0, sA0, sB0, sA1, sB1);
+                step(nb, k0 + 1, sA1, sB1, sA0, sB0);
+            }
+            if (nk - nk_main > 0) step(nb, nk_main, sA0, sB0, sA1, sB1);
         }
-        // The last nk % 5 stages start again at unit 0.
-        const int rem = nk - nk_main;
-        if (rem > 0) step5(nk_main, u0, u1, u2, u3, u4);
-        if (rem > 1) step5(nk_main + 1, u2, u3, u4, u0, u1);
-        if (rem > 2) step5(nk_main + 2, u4, u0, u1, u2, u3);
-        if (rem > 3) step5(nk_main + 3, u1, u2, u3, u4, u0);
-    } else if (NSLOT == 3) {
-        issue(0, sA0, sB0);
-        issue(1, sA1, sB1);
-        PF_WAIT_VM(NLD);
-        __builtin_amdgcn_s_barrier();
-        read(sA0, sB0, 0, fa);
-        const int nk_main = nk - nk % 3;
-        for (int k0 = 0; k0 < nk_main; k0 += 3) {
-            step3(k0, sA0, sB0, sA1, sB1, sA2, sB2);
-            step3(k0 + 1, sA1, sB1, sA2, sB2, sA0, sB0);
-            step3(k0 + 2, sA2, sB2, sA0, sB0, sA1, sB1);
+    };
+    // Token blocks of this wave that hold at least one row of the expert:
+    // all of them except on the expert's last, partly filled tile.
+    {
+        using std::integral_constant;
+        const int vh = min(max(row_end - row0 - wm * (BM / 2), 0), BM / 2);
+        const int nvb = __builtin_amdgcn_readfirstlane((vh + 31) / 32);
+        if (nvb == 0) {
+            run(integral_constant<int, 0>{});
+        } else if (nvb == 1) {
+            run(integral_constant<int, 1>{});
+        } else if constexpr (NTB > 3) {
+            if (nvb == 2)
+                run(integral_constant<int, 2>{});
+            else if (nvb == 3)
+                run(integral_constant<int, 3>{});
+            else
+                run(integral_constant<int, NTB>{});
+        } else {
+            run(integral_constant<int, NTB>{});
         }
-        // The last nk % 3 stages start again at slot 0.
-        if (nk - nk_main > 0) step3(nk_main, sA0, sB0, sA1, sB1, sA2, sB2);
-        if (nk - nk_main > 1) step3(nk_main + 1, sA1, sB1, sA2, sB2, sA0, sB0);
-    } else {
-        issue(0, sA0, sB0);
-        issue(1, sA1, sB1);
-        PF_WAIT_VM(NLD);
-        __builtin_amdgcn_s_barrier();
-        read(sA0, sB0, 0, fa);
-        const int nk_main = nk - nk % 2;
-        for (int k0 = 0; k0 < nk_main; k0 += 2) {
-            step(k0, sA0, sB0, sA1, sB1);
-            step(k0 + 1, sA1, sB1, sA0, sB0);
-        }
-        if (nk - nk_main > 0) step(nk_main, sA0, sB0, sA1, sB1);
     }
     PF_WAIT_VM(0);
     PF_WAIT_LGKM0();
