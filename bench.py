@@ -259,7 +259,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="mixtral_decode")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-chunk", type=int, default=2048)
