@@ -1,6 +1,6 @@
 """MoE-layer forward throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config mixtral_decode]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--config mixtral_decode]
 
 One step is one moe_forward call (router, dispatch, grouped SwiGLU FFN,
 combine) over one batch of seeded synthetic tokens whose inputs and weights
