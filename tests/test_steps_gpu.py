@@ -135,3 +135,43 @@ def test_ffn_and_combine_steps(orc, name, T, d, F):
     say(f"    h rel-L2 {err_h:.3e}  y rel-L2 {err_y:.3e}")
     tol = 1e-4 if dt == "f32" else 1e-2
     assert err_h <= tol and err_y <= tol
+
+
+# Expert group sizes whose last row tile is partly filled at every 32-row
+# boundary: with 256-row tiles (T * K >= 512 E) each wave row of the tile
+# holds 0 to 4 token blocks with rows, with 128-row tiles 0 to 2.  F = 320 also
+# leaves the last weight tile of the first GEMM partly filled, and these small
+# grids run the second GEMM's k-split units.
+@pytest.mark.parametrize("name,T,E,sizes", [
+    ("tiles256", 1600, 6, [289, 447, 97, 480, 1, 129]),
+    ("tiles128", 300, 8, [1, 32, 33, 64, 65, 96, 97, 205]),
+])
+def test_ffn_partial_tiles(orc, name, T, E, sizes):
+    """moe_expert_ffn on groups of chosen sizes against the oracle's expert,
+    row by row, with the error bound checked group by group."""
+    import torch
+    K, d, F = 2, 256, 320
+    say(f"[case] partial tiles {name} T={T} E={E} sizes={sizes}")
+    cfg = scaled(CONFIGS["mixtral_prefill"], T=T, d=d, F=F, E=E, K=K, dtype="bf16")
+    inp = datagen.make_inputs(cfg)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(sizes)
+    S = int(offsets[-1])
+    assert S <= T * K
+    src = np.arange(T * K) % T
+    x_perm = inp["x"][src]
+    p = moe.problem(T, d, E, K, F, "bf16")
+    act = _empty((T * K, F), torch.bfloat16)
+    h = _empty((T * K, d), torch.bfloat16)
+    ws = _empty((moe.moe_expert_ffn_workspace_size(p),), torch.uint8)
+    moe.moe_expert_ffn(p, to_device(x_perm, "bf16"), _t(offsets), to_device(inp["w1"], "bf16"),
+                       to_device(inp["w3"], "bf16"), to_device(inp["w2"], "bf16"), act, h, ws)
+    torch.cuda.synchronize()
+    h_gpu = y_as_f64(to_host(h, "bf16"), "bf16")[:S]
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        ref = np.stack([orc.expert(inp["x"][src[r]], inp["w1"][e], inp["w3"][e], inp["w2"][e]) for r in range(r0, r1)])
+        err = np.linalg.norm(h_gpu[r0:r1] - ref) / np.linalg.norm(ref)
+        assert np.isfinite(h_gpu[r0:r1]).all(), f"expert {e}: non-finite rows"
+        assert err <= 1e-2, f"expert {e} ({r1 - r0} rows): rel-L2 {err:.3e}"
+    say(f"    {E} groups within 1e-2")
