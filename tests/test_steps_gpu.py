@@ -138,7 +138,7 @@ def test_ffn_and_combine_steps(orc, name, T, d, F):
 
 
 # Expert group sizes whose last row tile is partly filled at every 32-row
-# boundary: with 256-row tiles (T * K >= 512 E) each wave row of the tile
+# boundary: with 256-row tiles (T * K >= 128 E) each wave row of the tile
 # holds 0 to 4 token blocks with rows, with 128-row tiles 0 to 2.  F = 320 also
 # leaves the last weight tile of the first GEMM partly filled, and these small
 # grids run the second GEMM's k-split units.
