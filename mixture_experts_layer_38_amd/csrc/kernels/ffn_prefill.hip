@@ -27,9 +27,10 @@
 // quarter before.  Other K use a generic variant further down.
 //
 // Order.  Workgroup b runs on XCD b % 8.  The tiles are listed expert by
-// expert in groups of PF_GM row tiles (row tile fastest inside a group), and
-// XCD x takes the x-th contiguous eighth of that list, so the tiles that run
-// together on one XCD share their token rows and weight rows in its L2.
+// expert in groups of at most PF_GM row tiles of one expert (row tile fastest
+// inside a group), and XCD x takes the x-th contiguous eighth of that list, so
+// the tiles that run together on one XCD share their token rows and weight
+// rows in its L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -59,7 +60,12 @@ __device__ __forceinline__ int pf_swz(int r) { return (r ^ (r >> 3)) & 7; }
 int prefill_max_mtiles(int n_rows, int E) { return n_rows / 128 + E + 1; }
 
 // One block; thread e cuts expert e's rows into bm-row tiles: *mt_count
-// row tiles, tile j of expert mt_expert[j] starting at grouped row mt_row0[j].
+// row tiles, tile j starting at grouped row mt_row0[j].  mt_expert[j] packs
+// the tile's expert (bits 0-10) and its place in the tile order's groups:
+// each expert's row tiles form ceil(n / PF_GM) groups of balanced sizes, so
+// that no group mixes experts (a group's weight tiles are then shared by all
+// of its row tiles); bits 11-13 hold the group's size - 1, bits 14-16 the
+// tile's position in it.
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int bm, int min_rows,
                                                        const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ mt_count,
@@ -101,9 +107,15 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int b
     int before = 0;
     for (int w = 0; w < wv; ++w) before += wave_tot[w];
     const int start = before + incl - nt;
-    if (e < E) {
+    if (e < E && nt > 0) {
+        const int ng = (nt + PF_GM - 1) / PF_GM;
+        const int base = nt / ng, extra = nt % ng;  // group g: base + (g < extra) tiles
+        const int big = extra * (base + 1);
         for (int j = 0; j < nt && start + j < max_mt; ++j) {
-            mt_expert[start + j] = e;
+            const int g = j < big ? j / (base + 1) : extra + (j - big) / base;
+            const int gsz = base + (g < extra ? 1 : 0);
+            const int g0 = g * base + min(g, extra);
+            mt_expert[start + j] = e | ((gsz - 1) << 11) | ((j - g0) << 14);
             mt_row0[start + j] = offsets[e] + j * bm;
         }
     }
@@ -111,20 +123,23 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int b
 }
 
 // Tile t of the grouped order: row tile mt (of expert e, rows [row0, row_end))
-// and weight tile nt.
+// and weight tile nt.  A group of g row tiles starting at row tile m0 owns
+// tiles [m0 n_nt, (m0 + g) n_nt), row tile fastest, so tile t lies in the
+// group of row tile t / n_nt.
 struct PfTile {
     int mt, nt, e, row0, row_end;
 };
 __device__ __forceinline__ PfTile pf_tile(int t, int n_mt, int n_nt, const int32_t* mt_expert,
                                           const int32_t* mt_row0, const int32_t* offsets, int n_rows) {
     PfTile r;
-    const int grp = t / (PF_GM * n_nt);
-    const int first = grp * PF_GM;
-    const int gsize = min(PF_GM, n_mt - first);
-    const int rem = t - grp * PF_GM * n_nt;
+    const int m = t / n_nt;
+    const int v = mt_expert[m];
+    const int gsize = ((v >> 11) & 7) + 1;
+    const int first = m - ((v >> 14) & 7);
+    const int rem = t - first * n_nt;
     r.mt = first + rem % gsize;
     r.nt = rem / gsize;
-    r.e = mt_expert[r.mt];
+    r.e = mt_expert[r.mt] & 0x7FF;
     r.row0 = mt_row0[r.mt];
     r.row_end = min(offsets[r.e + 1], n_rows);
     return r;
@@ -620,7 +635,6 @@ constexpr int PG_BN = 256;
 constexpr int PG_BK = 64;
 constexpr int PG_LDS = PG_BK + 8;  // padded LDS row (bf16 elements)
 constexpr int PG_THREADS = 512;
-constexpr int PG_GM = PF_GM;
 constexpr int PG_XCD = PF_XCD;
 constexpr size_t PG_TILE_ELEMS = (size_t)PG_BM * PG_LDS;
 constexpr size_t PG_LDS_BYTES = 4 * PG_TILE_ELEMS * sizeof(bf16);
@@ -643,15 +657,11 @@ __global__ __launch_bounds__(PG_THREADS) void ffn_prefill_generic_kernel(
     if (slot >= per_xcd) return;
     const int t = (blockIdx.x % PG_XCD) * per_xcd + slot;
     if (t >= tiles) return;
-    const int grp = t / (PG_GM * n_nt);
-    const int first = grp * PG_GM;
-    const int gsize = min(PG_GM, n_mt - first);
-    const int rem = t - grp * PG_GM * n_nt;
-    const int mt = first + rem % gsize;
-    const int nt = rem / gsize;
-    const int e = mt_expert[mt];
-    const int row0 = mt_row0[mt];
-    const int row_end = min(offsets[e + 1], n_rows);
+    const PfTile tl = pf_tile(t, n_mt, n_nt, mt_expert, mt_row0, offsets, n_rows);
+    const int nt = tl.nt;
+    const int e = tl.e;
+    const int row0 = tl.row0;
+    const int row_end = tl.row_end;
 
     bf16* sA = smem;                      // [2][PG_BM][PG_LDS]
     bf16* sB = smem + 2 * PG_TILE_ELEMS;  // [2][PG_BN][PG_LDS]
