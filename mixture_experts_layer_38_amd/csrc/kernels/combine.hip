@@ -16,7 +16,7 @@ namespace moe {
 // One thread per 16-byte vector of one output row: thread i handles token
 // i / (d / VEC), columns VEC * (i % (d / VEC)) ..; all loads of a thread are
 // independent, so short and long token counts both fill the chip.
-template <typename T>
+template <typename T, int KC>
 __global__ __launch_bounds__(256) void combine_kernel(int n_tok, int K, int d,
                                                      const T* __restrict__ h,
                                                      const int32_t* __restrict__ assign_row,
@@ -31,14 +31,31 @@ __global__ __launch_bounds__(256) void combine_kernel(int n_tok, int K, int d,
     float acc[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
-    for (int k = 0; k < K; ++k) {
-        const int r = assign_row[(size_t)t * K + k];
-        if ((unsigned)r >= (unsigned)(n_tok * K)) continue;  // dropped (-1)
-        const float wk = w[(size_t)t * K + k];
-        const u32x4 raw = load16(h + (size_t)r * d + c);
-        const T* v = reinterpret_cast<const T*>(&raw);
+    // Slots in chunks of KC: the chunk's row indices and weights, then all of
+    // its rows' loads, then the sums in slot order (so the result does not
+    // depend on KC).
+    for (int k0 = 0; k0 < K; k0 += KC) {
+        int r[KC];
+        float wk[KC];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[j] = fmaf(wk, to_f32(v[j]), acc[j]);
+        for (int q = 0; q < KC; ++q) {
+            const bool in = k0 + q < K;
+            r[q] = in ? assign_row[(size_t)t * K + k0 + q] : -1;
+            wk[q] = in ? w[(size_t)t * K + k0 + q] : 0.0f;
+        }
+        u32x4 raw[KC];
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+            const bool ok = (unsigned)r[q] < (unsigned)(n_tok * K);  // dropped slot: -1
+            raw[q] = load16_or_zero(h + (size_t)(ok ? r[q] : 0) * d + c, ok);
+        }
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+            if ((unsigned)r[q] >= (unsigned)(n_tok * K)) continue;
+            const T* v = reinterpret_cast<const T*>(&raw[q]);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) acc[j] = fmaf(wk[q], to_f32(v[j]), acc[j]);
+        }
     }
     u32x4 outv;
     T* o = reinterpret_cast<T*>(&outv);
@@ -157,12 +174,16 @@ hipError_t launch_combine(int T, int K, int d, int dtype, const void* h,
     const unsigned grid = (unsigned)((vecs + 255) / 256);
     if (dtype == MOE_DTYPE_F32)
         MOE_TIMED_LAUNCH(MOE_KERNEL_COMBINE, s,
-                         combine_kernel<float><<<grid, 256, 0, s>>>(T, K, d, (const float*)h,
-                                                                    assign_row, w, (float*)y));
+                         combine_kernel<float, 2><<<grid, 256, 0, s>>>(T, K, d, (const float*)h,
+                                                                       assign_row, w, (float*)y));
+    else if (K <= 2)
+        MOE_TIMED_LAUNCH(MOE_KERNEL_COMBINE, s,
+                         combine_kernel<bf16, 2><<<grid, 256, 0, s>>>(T, K, d, (const bf16*)h,
+                                                                      assign_row, w, (bf16*)y));
     else
         MOE_TIMED_LAUNCH(MOE_KERNEL_COMBINE, s,
-                         combine_kernel<bf16><<<grid, 256, 0, s>>>(T, K, d, (const bf16*)h,
-                                                                   assign_row, w, (bf16*)y));
+                         combine_kernel<bf16, 8><<<grid, 256, 0, s>>>(T, K, d, (const bf16*)h,
+                                                                      assign_row, w, (bf16*)y));
     return hipGetLastError();
 }
 
