@@ -263,13 +263,26 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // Four 16-row blocks per workgroup for the down projection: each token
-    // fragment (an L2 read of the long activation rows) feeds four MFMAs.
-    // Measured on the Mixtral-shaped decode batch: one block 26 us slower per
-    // layer than two, four 1.7 us faster than two.
+    // fragment (an L2 read of the long activation rows) feeds four MFMAs; two
+    // 128-wide chunks per iteration when they tile F exactly.  Measured on the
+    // Mixtral-shaped decode batch (per layer, each against two blocks with two
+    // chunks on the same box): four blocks with one chunk 2.75 us slower, four
+    // blocks with two chunks 0.6 us faster, two blocks with four chunks
+    // 2.75 us slower; with one chunk, one block was 26 us slower than two and
+    // four 1.7 us faster.
     dim3 g2((d + 4 * DC_ROWS - 1) / (4 * DC_ROWS), E);
-    MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
-                     ffn_decode_kernel<false, 1, 1, ALIGNED, 4><<<g2, DC_WAVES * kWave, 0, s>>>(
-                         n_rows, d, F, (const bf16*)act, nullptr, 1, offsets, (const bf16*)w2, nullptr, (bf16*)h));
+    bool two_f = false;
+    if constexpr (ALIGNED) two_f = F % (2 * DC_KCH) == 0;
+    if (two_f)
+        MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
+                         ffn_decode_kernel<false, 2, 1, ALIGNED, 4><<<g2, DC_WAVES * kWave, 0, s>>>(
+                             n_rows, d, F, (const bf16*)act, nullptr, 1, offsets, (const bf16*)w2, nullptr,
+                             (bf16*)h));
+    else
+        MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
+                         ffn_decode_kernel<false, 1, 1, ALIGNED, 4><<<g2, DC_WAVES * kWave, 0, s>>>(
+                             n_rows, d, F, (const bf16*)act, nullptr, 1, offsets, (const bf16*)w2, nullptr,
+                             (bf16*)h));
     return hipGetLastError();
 }
 
