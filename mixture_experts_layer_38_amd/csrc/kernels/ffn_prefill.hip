@@ -8,10 +8,13 @@
 // reduction dimension: act = SiLU(X W1^T) * (X W3^T) and h = act W2^T.
 //
 // Tiles.  A device-side plan (one tiny kernel) cuts every expert's rows into
-// 256-row tiles.  An output tile is 256 token rows x 256 weight rows; for
-// gate/up the 256 weight rows are 128 features of W1 and the same 128 of W3,
-// interleaved in 32-row blocks so that the SiLU-gate epilogue stays inside
-// each wave.  Four waves (one per SIMD) split the tile 2 x 2; a wave owns
+// 256-row tiles (128-row tiles when the groups average fewer than 128 rows;
+// the same code with half the token blocks).  On an expert's last, partly
+// filled tile each wave runs a copy of the main loop that multiplies only its
+// token blocks holding rows.  An output tile is 256 token rows x 256 weight
+// rows; for gate/up the 256 weight rows are 128 features of W1 and the same
+// 128 of W3, interleaved in 32-row blocks so that the SiLU-gate epilogue stays
+// inside each wave.  Four waves (one per SIMD) split the tile 2 x 2; a wave owns
 // 128 x 128 as 4 x 4 blocks of 32x32 accumulated in AGPRs with
 // v_mfma_f32_32x32x16_bf16 (weights as the first operand, so that each lane
 // ends with four consecutive output columns of one token).
