@@ -175,3 +175,36 @@ def test_ffn_partial_tiles(orc, name, T, E, sizes):
         assert np.isfinite(h_gpu[r0:r1]).all(), f"expert {e}: non-finite rows"
         assert err <= 1e-2, f"expert {e} ({r1 - r0} rows): rel-L2 {err:.3e}"
     say(f"    {E} groups within 1e-2")
+
+
+def test_ffn_high_expert_ids(orc):
+    """Tiled grouped FFN (d and F multiples of 64) on a few experts with high
+    ids among 1000, most experts empty: the tile plan's packed expert ids
+    cover the upper bits, and the groups' rows match the oracle."""
+    import torch
+    T, E, K, d, F = 1024, 1000, 2, 64, 128
+    groups = {0: 5, 513: 300, 700: 77, 999: 129}
+    say(f"[case] high expert ids T={T} E={E} groups={groups}")
+    cfg = scaled(CONFIGS["dsv3_routed"], T=T, d=d, F=F, E=E, K=K, dtype="bf16")
+    inp = datagen.make_inputs(cfg)
+    sizes = np.zeros(E, np.int64)
+    for e, n in groups.items():
+        sizes[e] = n
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(sizes)
+    S = int(offsets[-1])
+    src = np.arange(T * K) % T
+    p = moe.problem(T, d, E, K, F, "bf16")
+    act = _empty((T * K, F), torch.bfloat16)
+    h = _empty((T * K, d), torch.bfloat16)
+    ws = _empty((moe.moe_expert_ffn_workspace_size(p),), torch.uint8)
+    moe.moe_expert_ffn(p, to_device(inp["x"][src], "bf16"), _t(offsets), to_device(inp["w1"], "bf16"),
+                       to_device(inp["w3"], "bf16"), to_device(inp["w2"], "bf16"), act, h, ws)
+    torch.cuda.synchronize()
+    h_gpu = y_as_f64(to_host(h, "bf16"), "bf16")[:S]
+    for e in groups:
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        ref = np.stack([orc.expert(inp["x"][src[r]], inp["w1"][e], inp["w3"][e], inp["w2"][e]) for r in range(r0, r1)])
+        err = np.linalg.norm(h_gpu[r0:r1] - ref) / np.linalg.norm(ref)
+        assert err <= 1e-2, f"expert {e} ({r1 - r0} rows): rel-L2 {err:.3e}"
+    say(f"    {len(groups)} groups within 1e-2")
