@@ -335,12 +335,13 @@ void ffn_prefill_kernel(
     auto interleave = [&](auto nb, auto nv_c) __attribute__((always_inline)) {
         constexpr int NV = decltype(nv_c)::value;
         constexpr int NM = 4 * decltype(nb)::value;
+        constexpr int DM = NM > 0 ? NM : 1;  // a wave with no blocks has no MFMAs to spread over
         static_assert(NM == 0 || NV <= NM, "one load per MFMA at most");
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i < 4 + decltype(nb)::value) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (((i + 1) * NV) / NM > (i * NV) / NM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (((i + 1) * NV) / DM > (i * NV) / DM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
     // After the barrier: the last quarter's MFMAs, NV loads and the reads of
