@@ -37,7 +37,11 @@
  *    (fp32 or bf16); logits, probabilities, routing weights and biases are
  *    fp32; ids, counts, offsets and row maps are int32.
  *  - Non-finite inputs are outside the contract.
- *  - Calls on distinct workspaces are independent and re-entrant.
+ *  - Calls on distinct workspaces are independent and re-entrant.  The one
+ *    piece of process-wide state is the tracing hook moe_set_kernel_timer:
+ *    while it is armed, launches from every thread record into the same
+ *    event list (under a lock), so arm it only around single-threaded
+ *    measurements.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -261,7 +265,10 @@ moe_status moe_router_losses(const moe_problem* p, const float* logits, const fl
                              float* aux_topk, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- timing hook (tracing, not part of the layer) -------------------------
- * Kernels of the library, by id, for moe_set_kernel_timer / moe_kernel_name. */
+ * Kernels of the library, by id, for moe_set_kernel_timer / moe_kernel_name.
+ * MOE_KERNEL_FFN_GATE_UP and MOE_KERNEL_FFN_DOWN time a whole GEMM step of
+ * the expert FFN: every launch it takes (on large batches, the tiled GEMM,
+ * the small-expert launch and the k-split launches of the second GEMM). */
 enum {
     MOE_KERNEL_ROUTER = 0,
     MOE_KERNEL_DISPATCH_COUNT = 1,
@@ -281,13 +288,16 @@ enum {
 /* Name of kernel `kid` ("?" when out of range). */
 const char* moe_kernel_name(int kid);
 
-/* While set, each launch of kernel `kid` (on whatever stream it runs) is
+/* While set, each launch of kernel (or GEMM step) `kid`, on whatever stream it runs, is
  * bracketed by hipEventRecord(start_events[i]) / hipEventRecord(stop_events[i])
  * on that stream, for i = 0, 1, ... up to n_events - 1; later launches are not
  * recorded.  The events are hipEvent_t created by the caller.  Passing
  * n_events = 0 clears the hook.  Returns through *recorded (may be NULL) the
  * number of pairs recorded so far when called with n_events < 0 (query only).
- * Process-wide state: not for concurrent use from several threads. */
+ * Process-wide state, guarded by a lock: arming, querying and the recording
+ * itself are thread-safe, but launches from several threads while it is
+ * armed fill one list in whatever order they run.  While no timer is armed a
+ * launch only reads one atomic flag. */
 moe_status moe_set_kernel_timer(int kid, void* const* start_events, void* const* stop_events,
                                 int n_events, int* recorded);
 

@@ -35,6 +35,7 @@
 // the tiles that run together on one XCD share their token rows and weight
 // rows in its L2.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "../device_common.h"
@@ -874,6 +875,26 @@ size_t prefill_ws_bytes(int n_rows, int E, int d) {
     return prefill_plan_bytes(n_rows, E) + prefill_split_bytes(n_rows, E, d);
 }
 
+// The generic kernels take more dynamic LDS than the default limit.  The
+// attribute is raised once per device (std::call_once per device index, so
+// concurrent first calls from several threads are safe); a failure is kept
+// and returned by every later call on that device.
+constexpr int PG_MAX_DEVICES = 64;
+template <bool GATED>
+static hipError_t generic_lds_attr() {
+    static std::once_flag once[PG_MAX_DEVICES];
+    static hipError_t result[PG_MAX_DEVICES];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= PG_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev] {
+        result[dev] = hipFuncSetAttribute((const void*)ffn_prefill_generic_kernel<GATED>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)PG_LDS_BYTES);
+    });
+    return result[dev];
+}
+
 template <bool GATED>
 static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int max_mt, int bm,
                                       const bf16* A, const int32_t* rowmap, int topk,
@@ -882,22 +903,17 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
                                       const int32_t* offsets, const bf16* Wa, const bf16* Wb,
                                       bf16* out, float* part, hipStream_t s) {
     const long tiles = (long)max_mt * n_nt;
-    const int kid = GATED ? MOE_KERNEL_FFN_GATE_UP : MOE_KERNEL_FFN_DOWN;
     if (K % PF_BK == 0) {
         // the second GEMM may cut its last round into k ranges (K >= 4 stages)
         const int cpx = (!GATED && K / PF_BK >= 4) ? prefill_cpx() : 0;
         const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
         const unsigned sgrid = (unsigned)(PF_XCD * cpx);  // split units: at most cpx per XCD
         if (bm == 256)
-            MOE_TIMED_LAUNCH(kid, s,
-                             (ffn_prefill_kernel<GATED, 256, 5, false><<<grid, PF_THREADS, 0, s>>>(
-                                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out,
-                                 cpx, part)));
+            ffn_prefill_kernel<GATED, 256, 5, false><<<grid, PF_THREADS, 0, s>>>(
+                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
         else
-            MOE_TIMED_LAUNCH(kid, s,
-                             (ffn_prefill_kernel<GATED, 128, 3, false><<<grid, PF_THREADS, 0, s>>>(
-                                 n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out,
-                                 cpx, part)));
+            ffn_prefill_kernel<GATED, 128, 3, false><<<grid, PF_THREADS, 0, s>>>(
+                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess || cpx == 0 || GATED) return err;
         if (bm == 256)
@@ -917,17 +933,10 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)ffn_prefill_generic_kernel<GATED>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)PG_LDS_BYTES);
-        if (err != hipSuccess) return err;
-        attr_set = true;
-    }
-    MOE_TIMED_LAUNCH(kid, s,
-                     ffn_prefill_generic_kernel<GATED><<<grid, PG_THREADS, PG_LDS_BYTES, s>>>(
-                         n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out));
+    hipError_t aerr = generic_lds_attr<GATED>();
+    if (aerr != hipSuccess) return aerr;
+    ffn_prefill_generic_kernel<GATED><<<grid, PG_THREADS, PG_LDS_BYTES, s>>>(
+        n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out);
     return hipGetLastError();
 }
 
@@ -961,6 +970,9 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
                                                         mt_row0, small_count, small_list));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // The timing hook brackets each GEMM step as a whole: the tiled launch,
+    // the small-expert launch and (second GEMM) the k-split launches.
+    timer_before(MOE_KERNEL_FFN_GATE_UP, s);
     err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, (const bf16*)A,
                                     rowmap, topk, mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
                                     (const bf16*)w3, (bf16*)act, nullptr, s);
@@ -970,12 +982,19 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
                                    w3, act, s);
         if (err != hipSuccess) return err;
     }
+    timer_after(MOE_KERNEL_FFN_GATE_UP, s);
+    timer_before(MOE_KERNEL_FFN_DOWN, s);
     err = launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
                                      (const bf16*)act, nullptr, 1, mt_count, mt_expert, mt_row0, offsets,
                                      (const bf16*)w2, nullptr, (bf16*)h, part, s);
-    if (err != hipSuccess || !small) return err;
-    return launch_small_experts(false, E, n_rows, d, F, act, nullptr, 1, offsets, small_list, small_count, w2,
-                                nullptr, h, s);
+    if (err != hipSuccess) return err;
+    if (small) {
+        err = launch_small_experts(false, E, n_rows, d, F, act, nullptr, 1, offsets, small_list, small_count, w2,
+                                   nullptr, h, s);
+        if (err != hipSuccess) return err;
+    }
+    timer_after(MOE_KERNEL_FFN_DOWN, s);
+    return hipSuccess;
 }
 
 // A plain linear layer (one group of n_rows rows) on the second GEMM's

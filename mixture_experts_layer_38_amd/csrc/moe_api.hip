@@ -1,7 +1,9 @@
 // C ABI of the MoE layer (include/moe.h): argument checks, workspace layout,
 // and the order of launches.  Never allocates, never synchronises.
 #include <algorithm>
+#include <atomic>
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <stdint.h>
 #include <string.h>
 
@@ -10,6 +12,9 @@
 namespace moe {
 
 // ---- timing hook --------------------------------------------------------------
+// Process-wide tracing state.  While no timer is armed, a launch reads one
+// atomic and touches nothing else, so concurrent layer calls share no
+// mutable state; an armed timer's slots are updated under a mutex.
 namespace {
 struct TimerSlot {
     void* const* start = nullptr;
@@ -18,13 +23,19 @@ struct TimerSlot {
     int recorded = 0;
 };
 TimerSlot g_timer[MOE_KERNEL_COUNT];
+std::atomic<int> g_timer_armed{0};  // slots with n > 0
+std::mutex g_timer_mu;
 }  // namespace
 
 void timer_before(int kid, hipStream_t s) {
+    if (g_timer_armed.load(std::memory_order_acquire) == 0) return;
+    std::lock_guard<std::mutex> lk(g_timer_mu);
     TimerSlot& t = g_timer[kid];
     if (t.recorded < t.n) (void)hipEventRecord((hipEvent_t)t.start[t.recorded], s);
 }
 void timer_after(int kid, hipStream_t s) {
+    if (g_timer_armed.load(std::memory_order_acquire) == 0) return;
+    std::lock_guard<std::mutex> lk(g_timer_mu);
     TimerSlot& t = g_timer[kid];
     if (t.recorded < t.n) {
         (void)hipEventRecord((hipEvent_t)t.stop[t.recorded], s);
@@ -207,16 +218,19 @@ const char* moe_kernel_name(int kid) {
 moe_status moe_set_kernel_timer(int kid, void* const* start_events, void* const* stop_events,
                                 int n_events, int* recorded) {
     if (kid < 0 || kid >= MOE_KERNEL_COUNT) return MOE_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_timer_mu);
     TimerSlot& t = g_timer[kid];
     if (n_events < 0) {
         if (recorded) *recorded = t.recorded;
         return MOE_OK;
     }
     if (n_events > 0 && (!start_events || !stop_events)) return MOE_ERR_INVALID_ARG;
+    const bool was = t.n > 0, now = n_events > 0;
     t.start = start_events;
     t.stop = stop_events;
     t.n = n_events;
     t.recorded = 0;
+    if (now != was) g_timer_armed.fetch_add(now ? 1 : -1, std::memory_order_release);
     if (recorded) *recorded = 0;
     return MOE_OK;
 }

@@ -49,6 +49,6 @@ def test_chunked_forward(orc, cfg, chunk):
     assert np.array_equal(ids, dbg["topk_ids"].cpu().numpy())
     assert np.abs(dbg["topk_w"].cpu().numpy() - w).max() <= TOL_W
     ref = orc.dispatch(ids, cfg.E, -1)
-    err = check_output(orc, cfg, inp, ids, w, ref["assign_row"], to_host(y, cfg.dtype))
-    say(f"    output error {err:.3e}; workspace {ws.numel() / 2**20:.1f} MiB vs "
+    err, worst, _ = check_output(orc, cfg, inp, ids, w, ref["assign_row"], to_host(y, cfg.dtype))
+    say(f"    output error {err:.3e} (worst row {worst:.3e}); workspace {ws.numel() / 2**20:.1f} MiB vs "
         f"{moe.moe_workspace_size(p) / 2**20:.1f} MiB unchunked")

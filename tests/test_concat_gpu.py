@@ -5,8 +5,8 @@ order (a slot dropped by capacity is a block of zeros) and passed through one
 linear layer W_cat [d, K*d].  Up to 64 tokens take the weight-streaming
 kernel, which reads each slot's rows of h in place with its reduction split
 into parts; more tokens gather the concatenation and take the tiled GEMM.
-Reduced cases compare every element; the Mixtral-sized cases (the decode and
-the prefill batch) compare sampled tokens.
+Every case compares every element, the Mixtral-sized ones (the decode and
+the prefill batch) included, with a per-row bound next to the global one.
 """
 from __future__ import annotations
 
@@ -21,6 +21,7 @@ from tests.gpu_harness import say
 pytestmark = pytest.mark.gpu
 
 TOL_BF16_REL_L2 = 1e-2
+TOL_BF16_ROW = 2e-2   # per row: one bf16 rounding of y plus fp32 sums
 TOL_F32_REL_INF = 1e-4
 
 
@@ -63,6 +64,12 @@ def _run(orc, T, K, d, dtype, drop, seed, sample=None):
     if dtype == "bf16":
         err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
         assert err <= TOL_BF16_REL_L2, err
+        n_ref = np.linalg.norm(ref, axis=1)
+        live = n_ref > 0
+        assert np.all(got[~live] == 0.0), "a token with every slot dropped is not zero"
+        if live.any():
+            rel = np.linalg.norm(got - ref, axis=1)[live] / n_ref[live]
+            assert rel.max() <= TOL_BF16_ROW, (rel.max(), int(np.argmax(rel)))
     else:
         err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
         assert err <= TOL_F32_REL_INF, err
@@ -96,4 +103,4 @@ def test_combine_concat_all_dropped(orc, T):
 @pytest.mark.parametrize("T", [32, 8192])
 @pytest.mark.timeout(600)
 def test_combine_concat_mixtral_sized(orc, T):
-    _run(orc, T, 2, 4096, "bf16", 0.0, seed=T, sample=24)
+    _run(orc, T, 2, 4096, "bf16", 0.0, seed=T)
