@@ -1,14 +1,20 @@
 """MoE-layer forward throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--config mixtral_decode]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--only WORKLOAD]
 
-One step is one moe_forward call (router, dispatch, grouped SwiGLU FFN,
-combine) over one batch of seeded synthetic tokens whose inputs and weights
-are already resident in HBM.  The headline line is the Mixtral-8x7B-shaped
-decode step (T=32, d=4096, E=8, K=2, F=14336, bf16); the prefill step
-(T=8192, Zipf(1.2) routing skew) runs on the same resident weights and is
-reported in the "prefill" object.  The CPU oracle is timed on a bounded
-sample of the same workload on this host.
+One step is one pass of the whole hot path (router, dispatch, grouped SwiGLU
+FFN, combine; for the capacity-limited layer also the aux loss and one bias
+update) over one batch of seeded synthetic tokens whose inputs and weights are
+already resident in HBM.  The headline line is the Mixtral-8x7B-shaped decode
+step (T=32, d=4096, E=8, K=2, F=14336, bf16).  The prefill step (T=8192,
+Zipf(1.2) routing skew) runs on the same resident weights and is reported in
+the "prefill" object; the DeepSeek-V3-shaped layer (T=4096, d=7168, E=256,
+K=8, F=2048) and the capacity-limited layer (T=16384, d=2048, E=64, K=2,
+F=1408, C=512) in "dsv3_routed" and "capacity_top2".  Each carries the
+roofline of its dominant kernel and of the whole layer, against the datasheet
+peaks and against the achievable peaks that two microbenchmarks measure on the
+same GPU ("peaks").  The CPU oracle is timed on a bounded sample of the decode
+workload on this host.
 """
 from __future__ import annotations
 
@@ -63,9 +69,10 @@ def load_traffic(workload: str, kernel: str, family: str):
 
 
 def gate_up_algorithmic(cfg, counts_kept: np.ndarray):
-    """Algorithmic bytes and flops of one gate/up launch: the W1 and W3 rows of
-    every expert with at least one kept row, each read once, plus the grouped
-    token rows read and the activation rows written."""
+    """Algorithmic bytes and flops of one gate/up GEMM step: the W1 and W3 rows
+    of every expert with at least one kept row, each read once, plus the
+    grouped token rows read and the activation rows written.  The step's time
+    covers every launch it takes (tiled GEMM and small-expert launch)."""
     S = int(counts_kept.sum())
     active = int((counts_kept > 0).sum())
     b = cfg.elem_bytes
@@ -84,15 +91,34 @@ def layer_algorithmic(cfg, counts_kept: np.ndarray):
     return bytes_, flops
 
 
-def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use_graph: bool = True):
-    """Time `steps` forward passes (after `warmup` untimed ones), each one whole
-    layer over the resident batch.  With use_graph the pass is captured once in
+def make_pass(cfg, layer, x, bias, y):
+    """One pass of the whole hot path over the resident batch: the layer, and
+    for a workload with a bias-update step also the aux loss and one update of
+    the balancing bias (from the pass's counts and probability sums)."""
+    import torch
+    if cfg.alpha is None:
+        return lambda: layer.forward(x, bias, y=y)
+    extra = {"counts": torch.empty(cfg.E, dtype=torch.int32, device="cuda"),
+             "prob_sum": torch.empty(cfg.E, dtype=torch.float32, device="cuda")}
+    aux = torch.empty(1, dtype=torch.float32, device="cuda")
+    beta = torch.zeros(cfg.E, dtype=torch.float32, device="cuda")
+
+    def run():
+        layer.forward(x, bias, y=y, dbg=extra)
+        layer.aux_loss(extra["counts"], extra["prob_sum"], out=aux)
+        layer.bias_update(extra["counts"], cfg.alpha, beta)
+    return run
+
+
+def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use_graph: bool = False):
+    """Time `steps` passes of the whole hot path (after `warmup` untimed ones),
+    each over the resident batch.  With use_graph the pass is captured once in
     a HIP graph and replayed (the library's launches are capture-safe: no
     allocation, no memset, no host synchronisation).  The dominant kernel's
     launch time is then measured over `steps` eager passes with HIP events
     recorded on the kernel's own stream (outside the timed region); the same
     eager passes give the spread of the per-pass device time (HIP events
-    around each layer call: p10, median, p90)."""
+    around each pass: p10, median, p90)."""
     import torch
     import mixture_experts_layer_38_amd as moe
     y = torch.empty((cfg.T, cfg.d), dtype=layer.torch_dtype, device="cuda")
@@ -101,20 +127,21 @@ def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use
     torch.cuda.synchronize()
     kept = dbg["kept"].cpu().numpy()
     counts = dbg["counts"].cpu().numpy()
+    del dbg
+    one_pass = make_pass(cfg, layer, x, bias, y)
     if use_graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            layer.forward(x, bias, y=y)  # first launches set kernel attributes
+            one_pass()  # first launches set kernel attributes
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            layer.forward(x, bias, y=y)
+            one_pass()
         run = graph.replay
     else:
-        def run():
-            layer.forward(x, bias, y=y)
+        run = one_pass
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -134,7 +161,7 @@ def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use
     keep = moe.moe_set_kernel_timer(kernel, starts, stops)
     for i in range(steps):
         step_a[i].record()
-        layer.forward(x, bias, y=y)
+        one_pass()
         step_b[i].record()
     torch.cuda.synchronize()
     n_rec = moe.moe_kernel_timer_count(kernel)
@@ -145,6 +172,50 @@ def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use
     spread = {"p10": float(np.percentile(step_ms, 10)), "median": float(np.median(step_ms)),
               "p90": float(np.percentile(step_ms, 90)), "passes": int(steps)}
     return wall, float(np.mean(kern_ms)) if kern_ms else float("nan"), counts, kept, spread
+
+
+def workload_record(cfg, layer, x, bias, steps: int, warmup: int, use_graph: bool, peaks: dict):
+    """Throughput of one workload with the roofline of its dominant kernel (the
+    gate/up GEMM step) and of the whole layer.  The bound is the MFMA peak when
+    the gate/up step's arithmetic intensity is above the ridge point of the two
+    peaks, else HBM."""
+    wall, k_ms, counts, kept, spread = time_workload(cfg, layer, x, bias, steps, warmup, "ffn_gate_up", use_graph)
+    ms = wall / steps * 1e3
+    gb, gf = gate_up_algorithmic(cfg, kept)
+    lb, lf = layer_algorithmic(cfg, kept)
+    family = "decode" if cfg.T <= 64 else "prefill"
+    traffic = load_traffic(cfg.name, "ffn_gate_up", family)
+    if gf / gb > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        ach = gf / (k_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "ffn_gate_up", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": traffic, "kernel_ms": k_ms,
+                "algorithmic_flops": gf}
+        if peaks.get("mfma_bf16_TFs"):
+            roof["frac_of_achievable"] = ach / peaks["mfma_bf16_TFs"]
+        lay = {"mfma_frac": lf / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
+    else:
+        ach = gb / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "kernel_ms": k_ms,
+                "algorithmic_bytes": gb}
+        if peaks.get("hbm_read_GBs"):
+            roof["frac_of_achievable"] = ach / peaks["hbm_read_GBs"]
+        lay = {"hbm_frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if peaks.get("hbm_read_GBs"):
+            lay["hbm_frac_of_achievable"] = lb / (ms * 1e-3) / 1e9 / peaks["hbm_read_GBs"]
+    avg = cfg.T * cfg.K / cfg.E
+    lay.update(algorithmic_bytes=lb, algorithmic_flops=lf)
+    rec = {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} K={cfg.K} F={cfg.F} {cfg.dtype}"
+                       + (f" C={cfg.capacity}" if cfg.capacity >= 0 else ""),
+           "value": cfg.T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": steps,
+           "roofline": roof, "step_ms": spread, "layer": lay,
+           "routing": {"counts_max_over_avg": float(counts.max() / avg), "counts_min": int(counts.min()),
+                       "counts_max": int(counts.max()), "kept_rows": int(kept.sum()),
+                       "dropped_rows": int(counts.sum() - kept.sum()),
+                       "active_experts": int((kept > 0).sum())}}
+    if cfg.E <= 16:
+        rec["routing"]["counts"] = counts.tolist()
+    return rec
 
 
 def time_chunked(cfg, layer, x, bias, chunk: int, steps: int):
@@ -230,6 +301,17 @@ def time_variants(cfg, layer, x, bias, steps: int, concat: bool = True):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, min_seconds: float = 10.0, max_reps: int = 200):
     """The CPU oracle (fp64, OpenMP on this host's cores) on the same workload:
     whole forward passes of the first min(T, 32) tokens (routing, grouping,
@@ -250,9 +332,22 @@ def cpu_baseline(cfg, inp, min_seconds: float = 10.0, max_reps: int = 200):
         if dt >= min_seconds or reps >= max_reps:
             break
     return {"value": reps * n_tokens / dt, "unit": "tokens/s", "cores": orc.num_threads(),
-            "kind": "oracle", "seconds": dt,
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": dt,
             "sample": f"{reps} full forward passes of {n_tokens} tokens of {cfg.name} "
                       f"(router, routing, grouping, fp64 SwiGLU experts and combine)"}
+
+
+def measure_peaks() -> dict:
+    """Achievable HBM read rate and dense bf16 MFMA rate on this GPU
+    (libmoepeaks.so microbenchmarks), beside the datasheet peaks."""
+    from mixture_experts_layer_38_amd import peaks
+    gbs, blocks = peaks.hbm_read_gbs()
+    return {"hbm_read_GBs": gbs, "mfma_bf16_TFs": peaks.mfma_bf16_tfs(),
+            "datasheet": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFs": MFMA_BF16_PEAK_TFS},
+            "probes": f"stream read of 4 GiB (plain 16-byte loads, 8 in flight per thread, contiguous "
+                      f"32 KB pieces per workgroup; best of 1024-8192 workgroups: {blocks}); "
+                      "100000 rounds of 8 independent 32x32x16 bf16 MFMAs per wave on random "
+                      "register operands, 4 waves per SIMD"}
 
 
 def main():
@@ -260,11 +355,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="mixtral_decode")
+    ap.add_argument("--only", default=None, choices=[None, "mixtral_decode", "mixtral_prefill", "dsv3_routed",
+                                                     "capacity_top2"],
+                    help="time one workload only (its object becomes the line's headline fields)")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--other-steps", type=int, default=20, help="steps of the DeepSeek-V3-shaped and capacity layers")
     ap.add_argument("--prefill-chunk", type=int, default=2048)
-    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the routing/combine variants and router losses")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per pass instead of launching eagerly "
@@ -281,80 +379,88 @@ def main():
     from mixture_experts_layer_38_amd.configs import CONFIGS
     from mixture_experts_layer_38_amd.layer import MoELayer, to_device
 
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     moe.load()
-    cfg = CONFIGS[args.config]
-    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
-    inp = datagen.make_inputs(cfg)
-    layer = MoELayer.from_host(cfg, inp)
-    x = to_device(inp["x"], cfg.dtype)
-    bias = None if inp["logit_bias"] is None else torch.from_numpy(inp["logit_bias"]).cuda()
-    print("[bench] timing", file=sys.stderr, flush=True)
-    wall, k_ms, counts, kept, spread = time_workload(cfg, layer, x, bias, args.steps, args.warmup, "ffn_gate_up",
-                                                      args.graph)
-    ms_step = wall / args.steps * 1e3
-    tok_s = cfg.T * args.steps / wall
-    gb, gf = gate_up_algorithmic(cfg, kept)
-    lb, lf = layer_algorithmic(cfg, kept)
-    traffic = load_traffic(cfg.name, "ffn_gate_up", "decode" if cfg.T <= 64 else "prefill")
-    # the gate/up launch is bounded by the MFMA peak when its arithmetic
-    # intensity is above the ridge point of the two peaks, else by HBM
-    if gf / gb > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "mfma", "kernel": "ffn_gate_up", "achieved": gf / (k_ms * 1e-3) / 1e12,
-                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
-        roof.update(frac=roof["achieved"] / MFMA_BF16_PEAK_TFS, traffic=traffic, kernel_ms=k_ms,
-                    algorithmic_flops=gf)
-    else:
-        roof = {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": gb / (k_ms * 1e-3) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        roof.update(frac=roof["achieved"] / HBM_PEAK_GBS, traffic=traffic, kernel_ms=k_ms, algorithmic_bytes=gb)
+    want = (lambda n: args.only is None or args.only == n)
+    peaks_rec = {}
+    if not args.no_peaks:
+        log("measuring the achievable HBM read and bf16 MFMA rates")
+        peaks_rec = measure_peaks()
+    records = {}
+    cfg = CONFIGS["mixtral_decode"]
+    inp = None
+    if want("mixtral_decode") or want("mixtral_prefill"):
+        log("generating the Mixtral-shaped inputs")
+        inp = datagen.make_inputs(cfg)
+        layer = MoELayer.from_host(cfg, inp)
+        x = to_device(inp["x"], cfg.dtype)
+        if want("mixtral_decode"):
+            log("timing mixtral_decode")
+            records["mixtral_decode"] = workload_record(cfg, layer, x, None, args.steps, args.warmup, args.graph,
+                                                        peaks_rec)
+            if not args.no_variants:
+                log("timing the decode variants")
+                records["mixtral_decode"]["variants"] = time_variants(cfg, layer, x, None, 20, concat=True)
+        if want("mixtral_prefill"):
+            pcfg = CONFIGS["mixtral_prefill"]
+            pin = datagen.make_inputs(pcfg, with_experts=False)
+            player = MoELayer(pcfg.T, pcfg.d, pcfg.E, pcfg.K, pcfg.F, pcfg.dtype, layer.w_router,
+                              layer.w1, layer.w3, layer.w2, pcfg.capacity)
+            px = to_device(pin["x"], pcfg.dtype)
+            pb = torch.from_numpy(pin["logit_bias"]).cuda()
+            log("timing mixtral_prefill")
+            rec = workload_record(pcfg, player, px, pb, args.prefill_steps, 2, args.graph, peaks_rec)
+            rec["chunked"] = time_chunked(pcfg, player, px, pb, args.prefill_chunk, args.prefill_steps)
+            if not args.no_variants:
+                rec["variants"] = time_variants(pcfg, player, px, pb, 3)
+            records["mixtral_prefill"] = rec
+            del player, px
+        del layer, x
+        torch.cuda.empty_cache()
+    for name in ("dsv3_routed", "capacity_top2"):
+        if not want(name):
+            continue
+        ocfg = CONFIGS[name]
+        log(f"generating the {name} inputs")
+        oin = datagen.make_inputs(ocfg)
+        olayer = MoELayer.from_host(ocfg, oin)
+        ox = to_device(oin["x"], ocfg.dtype)
+        ob = None if oin["logit_bias"] is None else torch.from_numpy(oin["logit_bias"]).cuda()
+        del oin
+        log(f"timing {name}")
+        records[name] = workload_record(ocfg, olayer, ox, ob, args.other_steps, 3, args.graph, peaks_rec)
+        del olayer, ox, ob
+        torch.cuda.empty_cache()
+
+    head_name = args.only or "mixtral_decode"
+    head = records[head_name]
+    hcfg = CONFIGS[head_name]
+    steps = args.steps if head_name == "mixtral_decode" else (
+        args.prefill_steps if head_name == "mixtral_prefill" else args.other_steps)
     result = {
-        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} K={cfg.K} "
-                               f"F={cfg.F} {cfg.dtype}", "T": cfg.T, "d_model": cfg.d,
-                   "experts": cfg.E, "top_k": cfg.K, "d_ff": cfg.F, "capacity": cfg.capacity,
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": hcfg.dtype, "data": "synthetic",
+        "config": {"workload": head["workload"], "T": hcfg.T, "d_model": hcfg.d, "experts": hcfg.E,
+                   "top_k": hcfg.K, "d_ff": hcfg.F, "capacity": hcfg.capacity,
                    "launch": "hip graph replay" if args.graph else "eager"},
-        "roofline": roof,
-        "step_ms": spread,
-        "layer": {"hbm_frac": lb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                  "algorithmic_bytes": lb, "algorithmic_flops": lf,
-                  "counts": counts.tolist()},
+        "roofline": head["roofline"],
+        "step_ms": head["step_ms"],
+        "layer": head["layer"],
+        "routing": head["routing"],
     }
-    if not args.no_variants:
-        print("[bench] timing the variants", file=sys.stderr, flush=True)
-        result["variants"] = time_variants(cfg, layer, x, bias, 20, concat=cfg.dtype == "bf16")
-    if not args.no_prefill and cfg.name == "mixtral_decode":
-        pcfg = CONFIGS["mixtral_prefill"]
-        pin = datagen.make_inputs(pcfg, with_experts=False)
-        player = MoELayer(pcfg.T, pcfg.d, pcfg.E, pcfg.K, pcfg.F, pcfg.dtype, layer.w_router,
-                          layer.w1, layer.w3, layer.w2, pcfg.capacity)
-        px = to_device(pin["x"], pcfg.dtype)
-        pb = torch.from_numpy(pin["logit_bias"]).cuda()
-        print("[bench] timing prefill", file=sys.stderr, flush=True)
-        pwall, pk_ms, pcounts, pkept, pspread = time_workload(pcfg, player, px, pb, args.prefill_steps, 2,
-                                                              "ffn_gate_up", args.graph)
-        pgb, pgf = gate_up_algorithmic(pcfg, pkept)
-        plb, plf = layer_algorithmic(pcfg, pkept)
-        pms = pwall / args.prefill_steps * 1e3
-        result["prefill"] = {
-            "workload": f"{pcfg.name}: T={pcfg.T} Zipf({pcfg.zipf_s}) skew",
-            "value": pcfg.T * args.prefill_steps / pwall, "unit": "tokens/s", "ms_per_step": pms,
-            "steps": args.prefill_steps,
-            "roofline": {"bound": "mfma", "kernel": "ffn_gate_up",
-                         "achieved": pgf / (pk_ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
-                         "unit": "TFLOP/s", "frac": pgf / (pk_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
-                         "traffic": load_traffic(pcfg.name, "ffn_gate_up", "prefill"), "kernel_ms": pk_ms},
-            "step_ms": pspread,
-            "layer_mfma_frac": plf / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
-            "counts": pcounts.tolist(),
-            "chunked": time_chunked(pcfg, player, px, pb, args.prefill_chunk, args.prefill_steps),
-        }
-        if not args.no_variants:
-            result["prefill"]["variants"] = time_variants(pcfg, player, px, pb, 3)
-        del player, px
-    if not args.no_cpu:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+    if "variants" in head:
+        result["variants"] = head["variants"]
+    for name in ("mixtral_prefill", "dsv3_routed", "capacity_top2"):
+        if name in records and name != head_name:
+            key = "prefill" if name == "mixtral_prefill" else name
+            result[key] = records[name]
+    if peaks_rec:
+        result["peaks"] = peaks_rec
+    if not args.no_cpu and head_name == "mixtral_decode" and inp is not None:
+        log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(result), flush=True)
 

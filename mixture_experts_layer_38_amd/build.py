@@ -17,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe.so")
+PEAKS_SRC = os.path.join(CSRC, "peaks", "peaks.hip")
+PEAKS_LIB_PATH = os.path.join(HERE, "libmoepeaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
@@ -49,15 +51,18 @@ def _compile(src: str, verbose: bool) -> str:
 
 
 def build(verbose: bool = False) -> str:
+    """libmoe.so (the layer) and libmoepeaks.so (the measurement probes)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
+    srcs = sources() + [PEAKS_SRC]
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", LIB_PATH + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    peaks_obj = objs.pop()
+    for out, inputs in ((LIB_PATH, objs), (PEAKS_LIB_PATH, [peaks_obj])):
+        cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *inputs, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(out + ".tmp", out)
     return LIB_PATH
 
 

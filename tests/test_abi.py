@@ -171,3 +171,19 @@ def test_chunked_forward_checks():
     assert lib.moe_forward_chunked(P, 256, A, A, A, A, A, None, A, None, A, ws - 1, None) == WORKSPACE
     dbg = moe.MoEDebugOut(counts=A)
     assert lib.moe_forward_chunked(P, 256, A, A, A, A, A, None, A, ctypes.byref(dbg), A, ws, None) == INVALID
+
+
+def test_peaks_library_exports_every_declared_function():
+    """libmoepeaks.so (the measurement probes of include/moe_peaks.h) loads
+    and exports what its header declares; no kernel is launched."""
+    from mixture_experts_layer_38_amd import peaks
+    text = open(os.path.join(ROOT, "include", "moe_peaks.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(peak_[a-z_]+)\s*\(", text)))
+    assert len(names) == 6
+    lib = peaks.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.peak_mfma_flops(4, 1) == 4 * 4 * 8 * 2.0 * 32 * 32 * 16
+    assert lib.peak_stream_read(None, 1 << 20, 1, None, None) == 1  # refused on the host
+    assert lib.peak_mfma_loop(A, 3, 1, A, None) == 1                 # iters not a multiple of 4
