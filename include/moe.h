@@ -203,6 +203,25 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
                        const float* logit_bias, void* y, const moe_debug_out* dbg,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free whole layer, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same layer and arguments as moe_forward, except
+ * that the workspace is a static device array inside the library, one copy
+ * per GPU (MOE_NOALLOC_WS_BYTES bytes, held until the process ends; its
+ * address is looked up on the first call on each device).  The call itself
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library
+ * routine.  Problems whose moe_workspace_size exceeds MOE_NOALLOC_WS_BYTES
+ * (decode-sized batches fit: for example 64 tokens of a d = 7168, K = 8,
+ * F = 14336 layer need 22 MiB) return MOE_ERR_WORKSPACE before any launch.
+ * Every call on one GPU uses that GPU's one array, and nothing in it has to
+ * start at zero: calls whose work overlaps on one GPU (concurrent streams,
+ * several threads) race on it and must be serialised by the caller. */
+#define MOE_NOALLOC_WS_BYTES (32u << 20)
+moe_status moe_forward_noalloc(const moe_problem* p, const void* x, const void* w_router,
+                               const void* w1, const void* w3, const void* w2,
+                               const float* logit_bias, void* y, const moe_debug_out* dbg,
+                               void* stream);
+
 /* Chunked forward: [NOTES] §4.3 (chunked MoE for prefill: run the token block
  * in chunks to cap peak memory).  The same layer as moe_forward, run over
  * tokens [t0, t0 + chunk_tokens) one chunk after another on `stream`, with a

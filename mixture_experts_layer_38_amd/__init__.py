@@ -76,6 +76,7 @@ def _lib():
         "moe_expert_ffn": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [P, vp, vp, vp, vp, vp],
         "moe_forward": [P, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoEDebugOut), vp, sz, vp],
+        "moe_forward_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoEDebugOut), vp],
         "moe_aux_loss": [P, vp, vp, vp, vp],
         "moe_bias_update": [P, vp, f32, vp, vp],
         "moe_set_kernel_timer": [i32, vp, vp, i32, ctypes.POINTER(i32)],
@@ -192,6 +193,20 @@ def moe_forward(p, x, w_router, w1, w3, w2, logit_bias, y, ws, dbg: dict | None 
                               _ptr(w2), _ptr(logit_bias), _ptr(y),
                               ctypes.byref(d) if d is not None else None, _ptr(ws), ws_bytes,
                               _stream(stream)), "moe_forward")
+
+
+MOE_NOALLOC_WS_BYTES = 32 << 20
+
+
+def moe_forward_noalloc(p, x, w_router, w1, w3, w2, logit_bias, y, dbg: dict | None = None, stream=None):
+    """The layer on the library's static per-GPU workspace (no allocation)."""
+    d = None
+    if dbg:
+        d = MoEDebugOut(**{k: _ptr(v) for k, v in dbg.items()})
+    _check(_lib().moe_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3),
+                                      _ptr(w2), _ptr(logit_bias), _ptr(y),
+                                      ctypes.byref(d) if d is not None else None, _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_forward_chunked_workspace_size(p: MoEProblem, chunk_tokens: int) -> int:

@@ -187,6 +187,35 @@ static moe_status forward_launch(const moe_problem* p, const ForwardLayout& L, c
     return hip_status(err);
 }
 
+// ---- allocation-free forward ------------------------------------------------------
+// The workspace of moe_forward_noalloc: a file-scope device array, one copy
+// per GPU the library runs on (held until the process ends).  Host code never
+// uses its name as an address: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_WS_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+// Device address of the current device's copy of `scratch`.
+static hipError_t device_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    *out = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -364,6 +393,29 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     if (!aligned16(ws)) return MOE_ERR_ALIGNMENT;
     return forward_launch(p, L, x, w_router, w1, w3, w2, logit_bias, y, D, (char*)ws,
                           (hipStream_t)stream);
+}
+
+moe_status moe_forward_noalloc(const moe_problem* p, const void* x, const void* w_router, const void* w1,
+                               const void* w3, const void* w2, const float* logit_bias, void* y,
+                               const moe_debug_out* dbg, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    REQUIRE(x);
+    REQUIRE(w_router);
+    REQUIRE(w1);
+    REQUIRE(w3);
+    REQUIRE(w2);
+    REQUIRE(y);
+    OPTIONAL(logit_bias);
+    moe_debug_out none;
+    memset(&none, 0, sizeof none);
+    const moe_debug_out& D = dbg ? *dbg : none;
+    if ((st = check_debug(D)) != MOE_OK) return st;
+    const ForwardLayout L = forward_layout(p);
+    if (L.total > (size_t)MOE_NOALLOC_WS_BYTES) return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (device_scratch(&ws) != hipSuccess || !ws) return MOE_ERR_HIP;
+    return forward_launch(p, L, x, w_router, w1, w3, w2, logit_bias, y, D, (char*)ws, (hipStream_t)stream);
 }
 
 moe_status moe_forward_chunked_workspace_size(const moe_problem* p, int32_t chunk_tokens,

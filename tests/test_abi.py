@@ -187,3 +187,14 @@ def test_peaks_library_exports_every_declared_function():
     assert lib.peak_mfma_flops(4, 1) == 4 * 4 * 8 * 2.0 * 32 * 32 * 16
     assert lib.peak_stream_read(None, 1 << 20, 1, None, None) == 1  # refused on the host
     assert lib.peak_mfma_loop(A, 3, 1, A, None) == 1                 # iters not a multiple of 4
+
+
+def test_noalloc_refuses_oversized_problems_on_the_host():
+    """moe_forward_noalloc checks the problem's workspace against its static
+    array before it touches the GPU: an oversized problem is refused, so no
+    kernel is launched with these fake pointers."""
+    lib = moe.load()
+    p = moe.problem(8192, 4096, 8, 2, 14336, "bf16")
+    assert _ws(p) > moe.MOE_NOALLOC_WS_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(p), A, A, A, A, A, None, A, None, None) == WORKSPACE
+    assert lib.moe_forward_noalloc(ctypes.byref(p), None, A, A, A, A, None, A, None, None) == INVALID
