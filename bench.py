@@ -345,7 +345,7 @@ def measure_peaks() -> dict:
     return {"hbm_read_GBs": gbs, "mfma_bf16_TFs": peaks.mfma_bf16_tfs(),
             "datasheet": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFs": MFMA_BF16_PEAK_TFS},
             "probes": f"stream read of 4 GiB (plain 16-byte loads, 8 in flight per thread, contiguous "
-                      f"32 KB pieces per workgroup; best of 1024-8192 workgroups: {blocks}); "
+                      f"32 KB pieces per workgroup; best of 256-4096 workgroups: {blocks}); "
                       "100000 rounds of 8 independent 32x32x16 bf16 MFMAs per wave on random "
                       "register operands, 4 waves per SIMD"}
 

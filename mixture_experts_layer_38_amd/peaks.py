@@ -52,7 +52,7 @@ def _time(fn, reps: int) -> float:
     return ms[len(ms) // 2]
 
 
-def hbm_read_gbs(nbytes: int = 4 << 30, grids=(1024, 2048, 4096, 8192), reps: int = 10):
+def hbm_read_gbs(nbytes: int = 4 << 30, grids=(256, 512, 1024, 2048, 4096), reps: int = 10):
     """Achievable read rate in GB/s: one pass over an nbytes buffer (far larger
     than the L2 and the 256 MB last-level cache), the best over a few grid
     sizes.  Returns (GB/s, workgroups of the best grid)."""
