@@ -256,6 +256,28 @@ def _event_ms(fn, reps: int) -> float:
     return a.elapsed_time(b) / reps
 
 
+def _kernel_ms(kernel: str, fn, reps: int) -> float:
+    """Mean milliseconds of the library kernel `kernel` over reps calls of fn()
+    (HIP events recorded by the library's timing hook); NaN if it never ran."""
+    import torch
+    import mixture_experts_layer_38_amd as moe
+    fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for e in starts + stops:
+        e.record()
+    torch.cuda.synchronize()
+    keep = moe.moe_set_kernel_timer(kernel, starts, stops)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    n = moe.moe_kernel_timer_count(kernel)
+    moe.moe_set_kernel_timer(kernel, [], [])
+    del keep
+    return float(np.mean([starts[i].elapsed_time(stops[i]) for i in range(n)])) if n else float("nan")
+
+
 def time_variants(cfg, layer, x, bias, steps: int, concat: bool = True):
     """The layer's other forms on the same resident batch: the routing
     variants (bias for selection only, unweighted mean), the router
@@ -279,7 +301,17 @@ def time_variants(cfg, layer, x, bias, steps: int, concat: bool = True):
     a = torch.empty(1, dtype=torch.float32, device="cuda")
     ms = _event_ms(lambda: moe.moe_router_losses(p, dbg["logits"], bias, dbg["topk_ids"], dbg["counts"], z, a, ws),
                    steps)
-    out["router_losses"] = {"us_per_call": ms * 1e3}
+    # Inside the layer the routing kernel gathers both regularisers from its
+    # own softmax; what they add is the routing kernel's extra time plus (on
+    # the batched path) one small reduce kernel, both timed with HIP events.
+    with_l = {"z_loss": z, "aux_topk": a}
+    r0 = _kernel_ms("router", lambda: layer.forward(x, bias, y=y), steps)
+    r1 = _kernel_ms("router", lambda: layer.forward(x, bias, y=y, dbg=with_l), steps)
+    red = _kernel_ms("router_losses", lambda: layer.forward(x, bias, y=y, dbg=with_l), steps)
+    out["router_losses"] = {"us_per_call": (r1 - r0 + (red if red == red else 0.0)) * 1e3,
+                            "inside_layer": {"route_kernel_us": r0 * 1e3, "route_kernel_with_losses_us": r1 * 1e3,
+                                             "reduce_us": red * 1e3 if red == red else 0.0},
+                            "standalone_us_per_call": ms * 1e3}
     if concat:
         g = torch.Generator(device="cuda").manual_seed(11)
         S, dk = cfg.T * cfg.K, cfg.K * cfg.d

@@ -98,7 +98,9 @@ typedef struct {
 } moe_problem;
 
 /* Optional device outputs of moe_forward; any field may be NULL, in which
- * case the value lives only in the workspace.  Shapes as in the step calls. */
+ * case the value lives only in the workspace (z_loss and aux_topk are then
+ * not computed).  Shapes as in the step calls.  Pointers are 16-byte aligned,
+ * except the two scalars (4-byte aligned). */
 typedef struct {
     float* logits;        /* [T, E]  router scores x W_r (before the bias) */
     float* probs;         /* [T, E]  softmax over all experts of logits + bias */
@@ -110,6 +112,11 @@ typedef struct {
     int32_t* offsets;     /* [E + 1] */
     int32_t* assign_row;  /* [T * K] */
     int32_t* row_assign;  /* [T * K] */
+    /* Router regularisers of [NOTES] §3.2, gathered by the routing kernel from
+     * its own max and sum of exponentials (one fp32 each, as
+     * moe_router_losses defines them): */
+    float* z_loss;        /* (1/T) sum_t (log sum_e exp(logits[t,e]))^2 */
+    float* aux_topk;      /* E sum_e f_e P'_e over the chosen experts */
 } moe_debug_out;
 
 /* Human-readable name of a status. */
@@ -229,7 +236,9 @@ moe_status moe_forward_noalloc(const moe_problem* p, const void* x, const void* 
  * chunk).  Each token's routing and output are defined as in moe_forward.
  * Capacity must be unlimited (capacity < 0; a per-batch cap does not split
  * into chunks: MOE_ERR_UNSUPPORTED otherwise), and of `dbg` only the
- * per-token fields (logits, probs, topk_ids, topk_w) may be set. */
+ * per-token fields (logits, probs, topk_ids, topk_w) may be set (the batch
+ * sums prob_sum, counts, z_loss and aux_topk are refused with
+ * MOE_ERR_INVALID_ARG). */
 moe_status moe_forward_chunked_workspace_size(const moe_problem* p, int32_t chunk_tokens,
                                               size_t* bytes);
 moe_status moe_forward_chunked(const moe_problem* p, int32_t chunk_tokens, const void* x,

@@ -43,7 +43,7 @@ class MoEProblem(ctypes.Structure):
 class MoEDebugOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "probs", "prob_sum", "topk_ids", "topk_w", "counts", "kept", "offsets",
-        "assign_row", "row_assign")]
+        "assign_row", "row_assign", "z_loss", "aux_topk")]
 
 
 _LIB = None

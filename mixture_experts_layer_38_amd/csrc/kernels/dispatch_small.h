@@ -36,8 +36,9 @@ __device__ __forceinline__ int block_exscan_1024(int v, int* wave_tot, int* tota
 // or LDS) by a block of 1024 threads (thread e owns expert e in the scan;
 // E <= 1024).  hist and offs: 1024 ints of LDS each; wave_tot: 16 ints.
 // Integer adds commute, so the LDS histogram is exact; the ranks come from
-// ballots in flat order, never from an atomic.
-__device__ __forceinline__ void dispatch_small_block(
+// ballots in flat order, never from an atomic.  Returns the routed count of
+// expert threadIdx.x (0 for threads >= E).
+__device__ __forceinline__ int dispatch_small_block(
     int n, int E, int nbits, int capacity, const int32_t* ids, int32_t* __restrict__ counts,
     int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ assign_row,
     int32_t* __restrict__ row_assign, int* hist, int* offs, int* wave_tot) {
@@ -95,6 +96,7 @@ __device__ __forceinline__ void dispatch_small_block(
     }
     // Rows past the kept total S carry no assignment (disjoint from the rows above).
     for (int j = S + tid; j < n; j += 1024) row_assign[j] = -1;
+    return c;
 }
 
 }  // namespace moe

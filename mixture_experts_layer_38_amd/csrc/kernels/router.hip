@@ -36,10 +36,17 @@ constexpr int RG_KCH = 128;  // d chunk per gemm iteration
 // expert lane + 64 j.  flags: MOE_FLAG_BIAS_SELECT_ONLY (the bias steers the
 // choice only; probabilities and weights come from the unbiased scores),
 // MOE_FLAG_COMBINE_MEAN (every weight is 1/K).
+//
+// With `losses`, the router regularisers of the MoE notes §3.2 are gathered
+// from the same max and sum of exponentials: zacc (wave-uniform) adds the
+// token's squared log-sum-exp of the unbiased scores, and csum[j] adds the
+// routing probability (softmax of scores + bias over all experts) of expert
+// lane + 64 j when the token chose it.
 template <int MAXV>
 __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int K, const float* bias,
                                             int flags, float* probs_row, int32_t* ids_row,
-                                            float* w_row, float (&psum)[MAXV]) {
+                                            float* w_row, float (&psum)[MAXV], bool losses = false,
+                                            float* zacc = nullptr, float* csum = nullptr) {
     const int lane = lane_id();
     const bool sel_only = (flags & MOE_FLAG_BIAS_SELECT_ONLY) != 0;
     float v[MAXV];  // selection keys: scores + bias
@@ -78,6 +85,39 @@ __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int 
             if (probs_row) probs_row[e] = p;
         }
     }
+    // Regularisers: the unbiased log-sum-exp is the softmax's own when the
+    // softmax ran on the unbiased scores, and the routing probabilities are
+    // the softmax's own when it ran on the biased ones.
+    float mb = m, sb = s;
+    if (losses) {
+        float m0 = m, s0 = s;
+        if (bias && !sel_only) {
+            m0 = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < MAXV; ++j)
+                if (lane + j * kWave < E) m0 = fmaxf(m0, lg[j]);
+            m0 = wave_max(m0);
+            s0 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < MAXV; ++j)
+                if (lane + j * kWave < E) s0 += expf(lg[j] - m0);
+            s0 = wave_sum(s0);
+        }
+        if (bias && sel_only) {
+            mb = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < MAXV; ++j)
+                if (lane + j * kWave < E) mb = fmaxf(mb, v[j]);
+            mb = wave_max(mb);
+            sb = 0.0f;
+#pragma unroll
+            for (int j = 0; j < MAXV; ++j)
+                if (lane + j * kWave < E) sb += expf(v[j] - mb);
+            sb = wave_sum(sb);
+        }
+        const float lse = m0 + logf(s0);
+        *zacc += lse * lse;
+    }
     // Top-K: K rounds of a wave-wide arg-max over the experts not yet taken.
     // Order: larger value first; equal values (including -0 vs +0, which
     // compare equal) go to the lower expert index.
@@ -107,7 +147,15 @@ __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int 
                 bi = oi;
             }
         }
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+        if ((bi & (kWave - 1)) == lane) {
+            taken |= 1u << (bi / kWave);
+            if (losses) {
+                const float pc = expf(bv - mb) / sb;  // routing probability of the winner
+#pragma unroll
+                for (int j = 0; j < MAXV; ++j)
+                    if (j == bi / kWave) csum[j] += pc;
+            }
+        }
         float uw = bv;  // softmax input of the winner
         if (sel_only) {
             float mine = 0.0f;
@@ -132,18 +180,24 @@ __device__ __forceinline__ void route_token(const float (&lg)[MAXV], int E, int 
 // src holds nsplit slices [nsplit][T][E] of partial scores (nsplit = 1: the
 // scores themselves).  When logits_out is given, the summed scores are written
 // there.  psum_part (optional) receives this block's per-expert probability sums.
+// loss_part (optional): this block's router-regulariser partials, the
+// chosen-probability sums at [blockIdx.x][E] and the sum of squared
+// log-sum-exps at [gridDim.x * E + blockIdx.x] (router_losses_reduce_kernel
+// adds them up).
 template <int MAXV>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(
     int T, int E, int K, int flags, int nsplit, const float* __restrict__ src,
     float* __restrict__ logits_out, const float* __restrict__ bias, float* __restrict__ probs,
-    float* __restrict__ psum_part,
+    float* __restrict__ psum_part, float* __restrict__ loss_part,
     int32_t* __restrict__ ids, float* __restrict__ w) {
-    extern __shared__ float red[];  // [RT_THREADS / kWave][E]
+    extern __shared__ float red[];  // [RT_THREADS / kWave][E], then [RT_THREADS / kWave] z sums
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
-    float psum[MAXV];
+    const bool losses = loss_part != nullptr;
+    float psum[MAXV], csum[MAXV];
+    float zacc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < MAXV; ++j) psum[j] = 0.0f;
+    for (int j = 0; j < MAXV; ++j) psum[j] = csum[j] = 0.0f;
     const size_t slice = (size_t)T * E;
     for (int tt = wave; tt < RT_BT; tt += RT_THREADS / kWave) {
         const int t = blockIdx.x * RT_BT + tt;
@@ -169,19 +223,32 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
             lg[j] = acc;
         }
         route_token<MAXV>(lg, E, K, bias, flags, probs ? probs + (size_t)t * E : nullptr,
-                          ids + (size_t)t * K, w + (size_t)t * K, psum);
+                          ids + (size_t)t * K, w + (size_t)t * K, psum, losses, &zacc, csum);
     }
-    if (psum_part) {
+    // Per-block sums over the waves, in wave order (a fixed order).
+    auto block_sums = [&](const float (&acc)[MAXV], float* out) {
 #pragma unroll
         for (int j = 0; j < MAXV; ++j) {
             const int e = lane + j * kWave;
-            if (e < E) red[wave * E + e] = psum[j];
+            if (e < E) red[wave * E + e] = acc[j];
         }
         __syncthreads();
         for (int e = threadIdx.x; e < E; e += RT_THREADS) {
-            float acc = red[e];
-            for (int wv = 1; wv < RT_THREADS / kWave; ++wv) acc += red[wv * E + e];
-            psum_part[(size_t)blockIdx.x * E + e] = acc;
+            float a = red[e];
+            for (int wv = 1; wv < RT_THREADS / kWave; ++wv) a += red[wv * E + e];
+            out[(size_t)blockIdx.x * E + e] = a;
+        }
+        __syncthreads();
+    };
+    if (psum_part) block_sums(psum, psum_part);
+    if (losses) {
+        float* zred = red + (RT_THREADS / kWave) * E;
+        if (lane == 0) zred[wave] = zacc;
+        block_sums(csum, loss_part);
+        if (threadIdx.x == 0) {
+            float a = zred[0];
+            for (int wv = 1; wv < RT_THREADS / kWave; ++wv) a += zred[wv];
+            loss_part[(size_t)gridDim.x * E + blockIdx.x] = a;
         }
     }
 }
@@ -453,9 +520,13 @@ __global__ __launch_bounds__(1024) void route_dispatch_small_kernel(
     const float* __restrict__ bias, float* __restrict__ logits, float* __restrict__ probs,
     float* __restrict__ prob_sum, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ assign_row, int32_t* __restrict__ row_assign) {
+    int32_t* __restrict__ assign_row, int32_t* __restrict__ row_assign, float* __restrict__ z_loss,
+    float* __restrict__ aux_topk) {
     __shared__ float lgs[RS_MAXT * RS_MAXE];
     __shared__ float pw[16][RS_MAXE];
+    __shared__ float cw[16][RS_MAXE];
+    __shared__ float zw[16];
+    __shared__ double pe[RS_MAXE];
     __shared__ int sids[RS_MAXT * RS_MAXE];
     __shared__ int hist[1024];
     __shared__ int offs[1024];
@@ -469,13 +540,19 @@ __global__ __launch_bounds__(1024) void route_dispatch_small_kernel(
         if (logits) logits[i] = v;
     }
     __syncthreads();
-    float psum[1] = {0.0f};
+    const bool losses = z_loss || aux_topk;
+    float psum[1] = {0.0f}, csum[1] = {0.0f};
+    float zacc = 0.0f;
     for (int t = wave; t < T; t += 16) {
         float lg[1] = {lane < E ? lgs[t * E + lane] : 0.0f};
         route_token<1>(lg, E, K, bias, flags, probs ? probs + (size_t)t * E : nullptr, sids + t * K,
-                       w + (size_t)t * K, psum);
+                       w + (size_t)t * K, psum, losses, &zacc, csum);
     }
-    if (lane < E) pw[wave][lane] = psum[0];
+    if (lane < E) {
+        pw[wave][lane] = psum[0];
+        cw[wave][lane] = csum[0];
+    }
+    if (lane == 0) zw[wave] = zacc;
     __syncthreads();
     if (prob_sum && threadIdx.x < E) {
         double v = 0.0;
@@ -483,15 +560,38 @@ __global__ __launch_bounds__(1024) void route_dispatch_small_kernel(
         prob_sum[threadIdx.x] = (float)v;
     }
     for (int i = threadIdx.x; i < T * K; i += 1024) ids[i] = sids[i];
-    dispatch_small_block(T * K, E, nbits, capacity, sids, counts, kept, offsets, assign_row, row_assign,
-                         hist, offs, wave_tot);
+    const int cnt = dispatch_small_block(T * K, E, nbits, capacity, sids, counts, kept, offsets, assign_row,
+                                         row_assign, hist, offs, wave_tot);
+    if (losses) {
+        // aux_topk = E sum_e f_e P'_e and z_loss = mean lse^2, in double, in
+        // expert and wave order
+        if ((int)threadIdx.x < E) {
+            double ch = 0.0;
+            for (int wv = 0; wv < 16; ++wv) ch += (double)cw[wv][threadIdx.x];
+            pe[threadIdx.x] = (double)cnt / ((double)T * K) * (ch / (double)T);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            if (aux_topk) {
+                double a = 0.0;
+                for (int e = 0; e < E; ++e) a += pe[e];
+                *aux_topk = (float)((double)E * a);
+            }
+            if (z_loss) {
+                double z = 0.0;
+                for (int wv = 0; wv < 16; ++wv) z += (double)zw[wv];
+                *z_loss = (float)(z / (double)T);
+            }
+        }
+    }
 }
 
 hipError_t launch_route_dispatch_small(int T, int d, int E, int K, int flags, int capacity, const void* x,
                                        const void* w_router, const float* bias, float* logits,
                                        float* probs, float* prob_sum, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* kept, int32_t* offsets,
-                                       int32_t* assign_row, int32_t* row_assign, void* ws, hipStream_t s) {
+                                       int32_t* assign_row, int32_t* row_assign, float* z_loss,
+                                       float* aux_topk, void* ws, hipStream_t s) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     float* part = reinterpret_cast<float*>(ws);
@@ -506,7 +606,8 @@ hipError_t launch_route_dispatch_small(int T, int d, int E, int K, int flags, in
     MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER, s,
                      route_dispatch_small_kernel<<<1, 1024, 0, s>>>(T, E, K, flags, capacity, nbits, part, bias,
                                                                     logits, probs, prob_sum, ids, w, counts,
-                                                                    kept, offsets, assign_row, row_assign));
+                                                                    kept, offsets, assign_row, row_assign,
+                                                                    z_loss, aux_topk));
     return hipGetLastError();
 }
 
@@ -563,21 +664,27 @@ size_t router_ws_bytes(int T, int d, int E, int dtype) { return router_layout(T,
 
 template <int MAXV>
 static hipError_t launch_route_t(int T, int E, int K, int flags, int nsplit, const float* src, float* logits_out,
-                                 const float* bias, float* probs, float* psum_part, int32_t* ids,
-                                 float* w, hipStream_t s) {
+                                 const float* bias, float* probs, float* psum_part, float* loss_part,
+                                 int32_t* ids, float* w, hipStream_t s) {
     const int nblk = router_num_blocks(T, 0);
+    const size_t lds = ((size_t)(RT_THREADS / kWave) * E + RT_THREADS / kWave) * 4;
     MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER, s,
-                     route_kernel<MAXV><<<nblk, RT_THREADS, (size_t)(RT_THREADS / kWave) * E * 4, s>>>(
-                         T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, ids, w));
+                     route_kernel<MAXV><<<nblk, RT_THREADS, lds, s>>>(
+                         T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, loss_part, ids, w));
     return hipGetLastError();
 }
 
 static hipError_t launch_route(int T, int E, int K, int flags, int nsplit, const float* src, float* logits_out,
-                               const float* bias, float* probs, float* psum_part, int32_t* ids,
-                               float* w, hipStream_t s) {
-    if (E <= 64) return launch_route_t<1>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
-    if (E <= 256) return launch_route_t<4>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
-    return launch_route_t<16>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, ids, w, s);
+                               const float* bias, float* probs, float* psum_part, float* loss_part,
+                               int32_t* ids, float* w, hipStream_t s) {
+    if (E <= 64)
+        return launch_route_t<1>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, loss_part, ids,
+                                 w, s);
+    if (E <= 256)
+        return launch_route_t<4>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, loss_part, ids,
+                                 w, s);
+    return launch_route_t<16>(T, E, K, flags, nsplit, src, logits_out, bias, probs, psum_part, loss_part, ids, w,
+                              s);
 }
 
 template <int NEB>
@@ -589,7 +696,8 @@ static void launch_gemm_t(int T, int d, int E, int ns, const bf16* x, const bf16
 
 hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const void* x,
                          const void* w_router, const float* bias, float* logits, float* probs,
-                         float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s) {
+                         float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s,
+                         float* loss_part) {
     const RouterLayout L = router_layout(T, d, E, dtype);
     char* base = reinterpret_cast<char*>(ws);
     float* part = prob_sum ? reinterpret_cast<float*>(base + L.psum) : nullptr;
@@ -621,7 +729,7 @@ hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const
             T, d, E, (const float*)x, (const float*)w_router, logits);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    err = launch_route(T, E, K, flags, nsplit, src, logits_out, bias, probs, part, ids, w, s);
+    err = launch_route(T, E, K, flags, nsplit, src, logits_out, bias, probs, part, loss_part, ids, w, s);
     if (err != hipSuccess || !prob_sum) return err;
     psum_reduce_kernel<<<(E + 3) / 4, 256, 0, s>>>(router_num_blocks(T, dtype), E, part, prob_sum);
     return hipGetLastError();

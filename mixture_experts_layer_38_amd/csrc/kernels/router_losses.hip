@@ -7,7 +7,9 @@
 //              p = softmax over all E of logits + bias (the routing softmax).
 // Two kernels, no atomics: per-token work writes per-block partial sums (a
 // wave per token, 16 tokens per block, fixed order inside the block), then one
-// block reduces the partials in a fixed order in double.
+// block reduces the partials in a fixed order in double.  Inside the layer the
+// route kernel writes the same partials from its own softmax (one pass over
+// the scores), and only the reduce kernel runs here.
 #include <math.h>
 
 #include "../device_common.h"
@@ -123,6 +125,13 @@ __global__ __launch_bounds__(1024) void router_losses_reduce_kernel(
             *aux_topk = (float)((double)E * acc);
         }
     }
+}
+
+hipError_t launch_router_losses_reduce(int T, int E, int K, int nblk, const float* part, const int32_t* counts,
+                                       float* z_loss, float* aux_topk, hipStream_t s) {
+    MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER_LOSSES, s,
+                     router_losses_reduce_kernel<<<1, 1024, 0, s>>>(T, E, K, nblk, part, counts, z_loss, aux_topk));
+    return hipGetLastError();
 }
 
 hipError_t launch_router_losses(int T, int E, int K, const float* logits, const float* bias,

@@ -30,9 +30,13 @@ int router_num_blocks(int T, int dtype);
 // Workspace of the router: W_r^T and partial scores (bf16 scores from x) and
 // the per-block probability sums.
 size_t router_ws_bytes(int T, int d, int E, int dtype);
+// loss_part (optional, router_num_blocks(T) * (E + 1) floats): the route
+// kernel's per-block partials of the router regularisers, for
+// launch_router_losses_reduce.
 hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const void* x,
                          const void* w_router, const float* bias, float* logits, float* probs,
-                         float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s);
+                         float* prob_sum, int32_t* ids, float* w, void* ws, hipStream_t s,
+                         float* loss_part = nullptr);
 
 // Small batches (bf16, T <= 64, E <= 16): scores, routing and dispatch in two
 // launches, with the outputs of launch_router followed by launch_dispatch
@@ -43,7 +47,8 @@ hipError_t launch_route_dispatch_small(int T, int d, int E, int K, int flags, in
                                        const void* w_router, const float* bias, float* logits,
                                        float* probs, float* prob_sum, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* kept, int32_t* offsets,
-                                       int32_t* assign_row, int32_t* row_assign, void* ws, hipStream_t s);
+                                       int32_t* assign_row, int32_t* row_assign, float* z_loss,
+                                       float* aux_topk, void* ws, hipStream_t s);
 // ---- dispatch --------------------------------------------------------------
 size_t dispatch_ws_bytes(int T, int K, int E);
 hipError_t launch_dispatch(int T, int K, int E, int d, int dtype, int capacity,
@@ -70,6 +75,10 @@ hipError_t launch_small_experts(bool gated, int E, int n_rows, int N, int K, con
                                 const int32_t* ecount, const void* wa, const void* wb, void* out, hipStream_t s);
 // ---- router regularisers ----------------------------------------------------
 size_t router_losses_ws_bytes(int T, int E);
+// The final sums of the regularisers from nblk blocks of partials
+// ([nblk][E] chosen-probability sums, then [nblk] squared log-sum-exps).
+hipError_t launch_router_losses_reduce(int T, int E, int K, int nblk, const float* part, const int32_t* counts,
+                                       float* z_loss, float* aux_topk, hipStream_t s);
 hipError_t launch_router_losses(int T, int E, int K, const float* logits, const float* bias,
                                 const int32_t* ids, const int32_t* counts, float* z_loss,
                                 float* aux_topk, void* ws, hipStream_t s);

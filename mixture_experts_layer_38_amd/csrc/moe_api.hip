@@ -82,7 +82,7 @@ static size_t elem_bytes(const moe_problem* p) { return p->dtype == MOE_DTYPE_F3
 // ---- workspace layout of moe_forward ------------------------------------------------
 struct ForwardLayout {
     size_t logits, probs, prob_sum, ids, w, counts, kept, offsets, assign_row, row_assign;
-    size_t act, h, route_ws, disp_ws, ffn_ws, total;
+    size_t act, h, route_ws, disp_ws, ffn_ws, loss_part, total;
 };
 
 static ForwardLayout forward_layout(const moe_problem* p) {
@@ -111,6 +111,7 @@ static ForwardLayout forward_layout(const moe_problem* p) {
                                route_dispatch_small_ws_bytes(p->T, p->n_experts)));
     L.disp_ws = take(dispatch_ws_bytes(p->T, p->top_k, p->n_experts));
     L.ffn_ws = take(ffn_ws_bytes(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype));
+    L.loss_part = take((size_t)router_num_blocks(p->T, p->dtype) * (E + 1) * 4);
     L.total = o;
     return L;
 }
@@ -142,6 +143,8 @@ static moe_status check_debug(const moe_debug_out& D) {
     OPTIONAL(D.offsets);
     OPTIONAL(D.assign_row);
     OPTIONAL(D.row_assign);
+    if ((D.z_loss && ((uintptr_t)D.z_loss & 3u)) || (D.aux_topk && ((uintptr_t)D.aux_topk & 3u)))
+        return MOE_ERR_ALIGNMENT;
     return MOE_OK;
 }
 
@@ -162,16 +165,19 @@ static moe_status forward_launch(const moe_problem* p, const ForwardLayout& L, c
     void* act = base + L.act;
     void* h = base + L.h;
     hipError_t err;
+    const bool losses = D.z_loss || D.aux_topk;
     if (route_dispatch_small_ok(p->T, p->d_model, p->n_experts, p->top_k, p->dtype)) {
+        // routing, dispatch and the router regularisers in one block
         err = launch_route_dispatch_small(p->T, p->d_model, p->n_experts, p->top_k, (int)p->flags,
                                           p->capacity, x, w_router, logit_bias, logits, D.probs,
                                           D.prob_sum, ids, w, counts, kept, offsets, assign_row,
-                                          row_assign, base + L.route_ws, s);
+                                          row_assign, D.z_loss, D.aux_topk, base + L.route_ws, s);
         if (err != hipSuccess) return MOE_ERR_HIP;
     } else {
+        float* loss_part = losses ? (float*)(base + L.loss_part) : nullptr;
         err = launch_router(p->T, p->d_model, p->n_experts, p->top_k, p->dtype, (int)p->flags, x,
                             w_router, logit_bias, logits, D.probs, D.prob_sum, ids, w,
-                            base + L.route_ws, s);
+                            base + L.route_ws, s, loss_part);
         if (err != hipSuccess) return MOE_ERR_HIP;
         // The grouped token rows are never materialised: the first GEMM reads
         // token row_assign[r] / K for its grouped row r.
@@ -179,6 +185,11 @@ static moe_status forward_launch(const moe_problem* p, const ForwardLayout& L, c
                               nullptr, counts, kept, offsets, assign_row, row_assign, nullptr,
                               base + L.disp_ws, s);
         if (err != hipSuccess) return MOE_ERR_HIP;
+        if (losses) {
+            err = launch_router_losses_reduce(p->T, p->n_experts, p->top_k, router_num_blocks(p->T, p->dtype),
+                                              loss_part, counts, D.z_loss, D.aux_topk, s);
+            if (err != hipSuccess) return MOE_ERR_HIP;
+        }
     }
     err = launch_ffn(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype, x, row_assign,
                      offsets, w1, w3, w2, act, h, base + L.ffn_ws, s);
@@ -447,7 +458,8 @@ moe_status moe_forward_chunked(const moe_problem* p, int32_t chunk_tokens, const
     memset(&none, 0, sizeof none);
     const moe_debug_out& D = dbg ? *dbg : none;
     if ((st = check_debug(D)) != MOE_OK) return st;
-    if (D.prob_sum || D.counts || D.kept || D.offsets || D.assign_row || D.row_assign)
+    if (D.prob_sum || D.counts || D.kept || D.offsets || D.assign_row || D.row_assign || D.z_loss ||
+        D.aux_topk)
         return MOE_ERR_INVALID_ARG;  // only the per-token outputs are defined across chunks
     const int chunk = chunk_tokens < p->T ? chunk_tokens : p->T;
     moe_problem c = *p;

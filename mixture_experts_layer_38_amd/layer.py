@@ -56,12 +56,18 @@ class MoELayer:
                    to_device(inputs["w3"], dt, device), to_device(inputs["w2"], dt, device),
                    cfg.capacity, device, flags)
 
-    def alloc_debug(self) -> dict:
+    def alloc_debug(self, losses: bool = False) -> dict:
+        """Device buffers for every optional output of moe_forward; with
+        losses, also the two router regularisers (z_loss, aux_topk)."""
         import torch
         T, E, K = self.T, self.E, self.K
         dev = self.device
         f32, i32 = torch.float32, torch.int32
-        return {
+        extra = {}
+        if losses:
+            extra = {"z_loss": torch.full((1,), -1.0, dtype=f32, device=dev),
+                     "aux_topk": torch.full((1,), -1.0, dtype=f32, device=dev)}
+        return extra | {
             "logits": torch.empty((T, E), dtype=f32, device=dev),
             "probs": torch.empty((T, E), dtype=f32, device=dev),
             "prob_sum": torch.empty((E,), dtype=f32, device=dev),

@@ -35,8 +35,9 @@ def say(*a):
 
 
 def run_forward(cfg: MoEConfig, inp: dict, logit_bias: np.ndarray | None = None, repeat: int = 1,
-                flags: int = 0):
-    """moe_forward with every debug output; returns host arrays (and the layer)."""
+                flags: int = 0, losses: bool = False):
+    """moe_forward with every debug output (and the router regularisers with
+    losses); returns host arrays (and the layer)."""
     import torch
     layer = MoELayer.from_host(cfg, inp, flags=flags)
     x = to_device(inp["x"], cfg.dtype)
@@ -44,7 +45,7 @@ def run_forward(cfg: MoEConfig, inp: dict, logit_bias: np.ndarray | None = None,
     bias = None if lb is None else torch.from_numpy(np.ascontiguousarray(lb, np.float32)).cuda()
     outs = []
     for _ in range(repeat):
-        dbg = layer.alloc_debug()
+        dbg = layer.alloc_debug(losses)
         y = layer.forward(x, bias, dbg=dbg)
         torch.cuda.synchronize()
         host = {k: v.cpu().numpy() for k, v in dbg.items()}
