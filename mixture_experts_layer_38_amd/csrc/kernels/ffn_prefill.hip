@@ -40,6 +40,7 @@
 
 #include "../device_common.h"
 #include "../launch.h"
+#include "ffn_tiles.h"
 
 namespace moe {
 
@@ -47,19 +48,7 @@ constexpr int PF_BN = 256;          // weight rows per tile
 constexpr int PF_BK = 64;           // k per pipeline stage (128-byte tile rows)
 constexpr int PF_THREADS = 256;
 constexpr int PF_BM_MAX = 256;      // token rows per tile: 256, or 128 for small groups
-constexpr int PF_GM = 8;            // row tiles per group in the tile order
-constexpr int PF_XCD = 8;
 constexpr int PF_SMALL_MIN_E = 32;  // experts from which small groups leave the tiled GEMM
-
-// Swizzle of the eight 16-byte chunks of a 128-byte tile row: row r keeps
-// chunk c in slot c ^ pf_swz(r), so fragment reads of consecutive rows (one
-// chunk each) fall in distinct banks.
-__device__ __forceinline__ int pf_swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-// s_waitcnt immediate: vmcnt <= n, no wait on the other counters.
-#define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
-// s_waitcnt immediate: lgkmcnt == 0, no wait on the other counters.
-#define PF_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
 
 int prefill_max_mtiles(int n_rows, int E) { return n_rows / 128 + E + 1; }
 
@@ -124,29 +113,6 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int b
         }
     }
     if (e == E - 1) *mt_count = min(start + nt, max_mt);
-}
-
-// Tile t of the grouped order: row tile mt (of expert e, rows [row0, row_end))
-// and weight tile nt.  A group of g row tiles starting at row tile m0 owns
-// tiles [m0 n_nt, (m0 + g) n_nt), row tile fastest, so tile t lies in the
-// group of row tile t / n_nt.
-struct PfTile {
-    int mt, nt, e, row0, row_end;
-};
-__device__ __forceinline__ PfTile pf_tile(int t, int n_mt, int n_nt, const int32_t* mt_expert,
-                                          const int32_t* mt_row0, const int32_t* offsets, int n_rows) {
-    PfTile r;
-    const int m = t / n_nt;
-    const int v = mt_expert[m];
-    const int gsize = ((v >> 11) & 7) + 1;
-    const int first = m - ((v >> 14) & 7);
-    const int rem = t - first * n_nt;
-    r.mt = first + rem % gsize;
-    r.nt = rem / gsize;
-    r.e = mt_expert[r.mt] & 0x7FF;
-    r.row0 = mt_row0[r.mt];
-    r.row_end = min(offsets[r.e + 1], n_rows);
-    return r;
 }
 
 // Split of the last, partly filled round of tiles.  Each XCD runs its
