@@ -81,6 +81,19 @@ def gate_up_algorithmic(cfg, counts_kept: np.ndarray):
     return bytes_, flops
 
 
+def ffn_algorithmic(cfg, counts_kept: np.ndarray):
+    """Algorithmic bytes and flops of the whole expert FFN (both GEMMs, every
+    launch): W1, W3 and W2 of every expert with at least one kept row, each
+    read once, plus the grouped token rows read and the expert output rows
+    written (the activation rows between the GEMMs are an intermediate)."""
+    S = int(counts_kept.sum())
+    active = int((counts_kept > 0).sum())
+    b = cfg.elem_bytes
+    bytes_ = active * 3 * cfg.F * cfg.d * b + 2 * S * cfg.d * b
+    flops = 2.0 * S * 3 * cfg.d * cfg.F
+    return bytes_, flops
+
+
 def layer_algorithmic(cfg, counts_kept: np.ndarray):
     """Algorithmic bytes and flops of the whole layer (router + experts)."""
     S = int(counts_kept.sum())
@@ -174,20 +187,23 @@ def time_workload(cfg, layer, x, bias, steps: int, warmup: int, kernel: str, use
     return wall, float(np.mean(kern_ms)) if kern_ms else float("nan"), counts, kept, spread
 
 
-def workload_record(cfg, layer, x, bias, steps: int, warmup: int, use_graph: bool, peaks: dict):
-    """Throughput of one workload with the roofline of its dominant kernel (the
-    gate/up GEMM step) and of the whole layer.  The bound is the MFMA peak when
-    the gate/up step's arithmetic intensity is above the ridge point of the two
-    peaks, else HBM."""
-    wall, k_ms, counts, kept, spread = time_workload(cfg, layer, x, bias, steps, warmup, "ffn_gate_up", use_graph)
+def workload_record(cfg, layer, x, bias, steps: int, warmup: int, use_graph: bool, peaks: dict,
+                    kernel: str = "ffn_gate_up"):
+    """Throughput of one workload with the roofline of its dominant kernel and
+    of the whole layer.  The dominant kernel is the gate/up GEMM (kernel
+    "ffn_gate_up"), or the whole expert FFN ("ffn": both GEMMs with every
+    launch, the small expert groups on the auxiliary stream included).  The
+    bound is the MFMA peak when its arithmetic intensity is above the ridge
+    point of the two peaks, else HBM."""
+    wall, k_ms, counts, kept, spread = time_workload(cfg, layer, x, bias, steps, warmup, kernel, use_graph)
     ms = wall / steps * 1e3
-    gb, gf = gate_up_algorithmic(cfg, kept)
+    gb, gf = (ffn_algorithmic if kernel == "ffn" else gate_up_algorithmic)(cfg, kept)
     lb, lf = layer_algorithmic(cfg, kept)
     family = "decode" if cfg.T <= 64 else "prefill"
-    traffic = load_traffic(cfg.name, "ffn_gate_up", family)
+    traffic = load_traffic(cfg.name, kernel, family)
     if gf / gb > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
         ach = gf / (k_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "ffn_gate_up", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS,
+        roof = {"bound": "mfma", "kernel": kernel, "achieved": ach, "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": traffic, "kernel_ms": k_ms,
                 "algorithmic_flops": gf}
         if peaks.get("mfma_bf16_TFs"):
@@ -195,7 +211,7 @@ def workload_record(cfg, layer, x, bias, steps: int, warmup: int, use_graph: boo
         lay = {"mfma_frac": lf / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
     else:
         ach = gb / (k_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": ach, "peak": HBM_PEAK_GBS,
+        roof = {"bound": "hbm", "kernel": kernel, "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "kernel_ms": k_ms,
                 "algorithmic_bytes": gb}
         if peaks.get("hbm_read_GBs"):
@@ -462,7 +478,8 @@ def main():
         ob = None if oin["logit_bias"] is None else torch.from_numpy(oin["logit_bias"]).cuda()
         del oin
         log(f"timing {name}")
-        records[name] = workload_record(ocfg, olayer, ox, ob, args.other_steps, 3, args.graph, peaks_rec)
+        records[name] = workload_record(ocfg, olayer, ox, ob, args.other_steps, 3, args.graph, peaks_rec,
+                                        kernel="ffn")
         del olayer, ox, ob
         torch.cuda.empty_cache()
 

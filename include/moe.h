@@ -294,9 +294,10 @@ moe_status moe_router_losses(const moe_problem* p, const float* logits, const fl
 
 /* ---- timing hook (tracing, not part of the layer) -------------------------
  * Kernels of the library, by id, for moe_set_kernel_timer / moe_kernel_name.
- * MOE_KERNEL_FFN_GATE_UP and MOE_KERNEL_FFN_DOWN time a whole GEMM step of
- * the expert FFN: every launch it takes (on large batches, the tiled GEMM,
- * the small-expert launch and the k-split launches of the second GEMM). */
+ * MOE_KERNEL_FFN times the whole expert FFN (both GEMMs, every launch).
+ * MOE_KERNEL_FFN_GATE_UP and MOE_KERNEL_FFN_DOWN time one GEMM step each,
+ * with every launch it takes (on large batches, the tiled GEMM, the
+ * small-expert launch and the k-split launches of the second GEMM). */
 enum {
     MOE_KERNEL_ROUTER = 0,
     MOE_KERNEL_DISPATCH_COUNT = 1,
@@ -310,7 +311,8 @@ enum {
     MOE_KERNEL_BIAS_UPDATE = 9,
     MOE_KERNEL_FFN_PLAN = 10,
     MOE_KERNEL_ROUTER_LOSSES = 11,
-    MOE_KERNEL_COUNT = 12
+    MOE_KERNEL_FFN = 12,
+    MOE_KERNEL_COUNT = 13
 };
 
 /* Name of kernel `kid` ("?" when out of range). */

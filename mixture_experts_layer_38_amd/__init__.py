@@ -23,7 +23,7 @@ MOE_FLAG_BIAS_SELECT_ONLY, MOE_FLAG_COMBINE_MEAN = 1, 2
 KERNEL_IDS = {
     "router": 0, "dispatch_count": 1, "dispatch_scan": 2, "dispatch_scatter": 3,
     "dispatch_gather": 4, "ffn_gate_up": 5, "ffn_down": 6, "combine": 7, "aux_loss": 8,
-    "bias_update": 9, "ffn_plan": 10, "router_losses": 11,
+    "bias_update": 9, "ffn_plan": 10, "router_losses": 11, "ffn": 12,
 }
 
 

@@ -88,9 +88,10 @@ size_t ffn_ws_bytes(int T, int K, int E, int d, int /*F*/, int dtype) {
     return prefill_ws_bytes(T * K, E, d);
 }
 
-hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* A,
-                      const int32_t* rowmap, const int32_t* offsets, const void* w1,
-                      const void* w3, const void* w2, void* act, void* h, void* ws, hipStream_t s) {
+static hipError_t launch_ffn_paths(int T, int K, int E, int d, int F, int dtype, const void* A,
+                                   const int32_t* rowmap, const int32_t* offsets, const void* w1,
+                                   const void* w3, const void* w2, void* act, void* h, void* ws,
+                                   hipStream_t s) {
     const int n = T * K;
     if (dtype == MOE_DTYPE_F32) {
         const size_t n1 = (size_t)n * F, n2 = (size_t)n * d;
@@ -109,6 +110,16 @@ hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* 
     if (use_decode(T, dtype))
         return launch_ffn_decode(n, E, d, F, A, rowmap, K, offsets, w1, w3, w2, act, h, s);
     return launch_ffn_prefill(n, E, d, F, A, rowmap, K, offsets, w1, w3, w2, act, h, ws, s);
+}
+
+// The expert FFN as one timed step (MOE_KERNEL_FFN): every launch of both GEMMs.
+hipError_t launch_ffn(int T, int K, int E, int d, int F, int dtype, const void* A,
+                      const int32_t* rowmap, const int32_t* offsets, const void* w1,
+                      const void* w3, const void* w2, void* act, void* h, void* ws, hipStream_t s) {
+    timer_before(MOE_KERNEL_FFN, s);
+    const hipError_t err = launch_ffn_paths(T, K, E, d, F, dtype, A, rowmap, offsets, w1, w3, w2, act, h, ws, s);
+    if (err == hipSuccess) timer_after(MOE_KERNEL_FFN, s);
+    return err;
 }
 
 }  // namespace moe

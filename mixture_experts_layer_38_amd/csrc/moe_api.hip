@@ -251,7 +251,7 @@ const char* moe_kernel_name(int kid) {
     static const char* names[MOE_KERNEL_COUNT] = {
         "router", "dispatch_count", "dispatch_scan", "dispatch_scatter", "dispatch_gather",
         "ffn_gate_up", "ffn_down", "combine", "aux_loss", "bias_update", "ffn_plan",
-        "router_losses"};
+        "router_losses", "ffn"};
     return (kid >= 0 && kid < MOE_KERNEL_COUNT) ? names[kid] : "?";
 }
 
