@@ -461,6 +461,7 @@ def main():
             log("timing mixtral_prefill")
             rec = workload_record(pcfg, player, px, pb, args.prefill_steps, 2, args.graph, peaks_rec)
             rec["chunked"] = time_chunked(pcfg, player, px, pb, args.prefill_chunk, args.prefill_steps)
+            rec["chunked_4096"] = time_chunked(pcfg, player, px, pb, 4096, args.prefill_steps)
             if not args.no_variants:
                 rec["variants"] = time_variants(pcfg, player, px, pb, 3)
             records["mixtral_prefill"] = rec

@@ -26,8 +26,9 @@
 
 namespace moe {
 
-constexpr int RT_BT = 8;  // tokens per route workgroup (two per wave)
+constexpr int RT_TPW = 4;                       // tokens per route wave
 constexpr int RT_THREADS = 256;
+constexpr int RT_BT = RT_TPW * RT_THREADS / 64;  // tokens per route workgroup
 constexpr int RG_KCH = 128;  // d chunk per gemm iteration
 
 // ---- route ---------------------------------------------------------------------
@@ -198,31 +199,50 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
     float zacc = 0.0f;
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) psum[j] = csum[j] = 0.0f;
+    // Wave w routes tokens blockIdx.x * RT_BT + w * RT_TPW + [0, RT_TPW): the
+    // scores of all of them are loaded first (every load in flight at once),
+    // then the tokens are routed in order.
     const size_t slice = (size_t)T * E;
-    for (int tt = wave; tt < RT_BT; tt += RT_THREADS / kWave) {
-        const int t = blockIdx.x * RT_BT + tt;
-        if (t >= T) break;
-        float lg[MAXV];
+    const int t0 = blockIdx.x * RT_BT + wave * RT_TPW;
+    float lgs[RT_TPW][MAXV];
+#pragma unroll
+    for (int i = 0; i < RT_TPW; ++i) {
+        const int t = min(t0 + i, T - 1);
 #pragma unroll
         for (int j = 0; j < MAXV; ++j) {
             const int e = lane + j * kWave;
-            float acc = 0.0f;
-            if (e < E) {
-                // slices in ascending order; loads issued eight at a time
-                const float* p = src + (size_t)t * E + e;
-                for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
-                    float v8[8];
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) v8[q] = sp0 + q < nsplit ? p[(size_t)(sp0 + q) * slice] : 0.0f;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        if (sp0 + q < nsplit) acc = (sp0 + q == 0) ? v8[q] : acc + v8[q];
-                }
-                if (logits_out) logits_out[(size_t)t * E + e] = acc;
-            }
-            lg[j] = acc;
+            lgs[i][j] = e < E ? src[(size_t)t * E + e] : 0.0f;
         }
-        route_token<MAXV>(lg, E, K, bias, flags, probs ? probs + (size_t)t * E : nullptr,
+    }
+    // further slices of the scores, added in slice order
+    for (int sp = 1; sp < nsplit; ++sp) {
+        float v[RT_TPW][MAXV];
+#pragma unroll
+        for (int i = 0; i < RT_TPW; ++i) {
+            const int t = min(t0 + i, T - 1);
+#pragma unroll
+            for (int j = 0; j < MAXV; ++j) {
+                const int e = lane + j * kWave;
+                v[i][j] = e < E ? src[(size_t)sp * slice + (size_t)t * E + e] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RT_TPW; ++i)
+#pragma unroll
+            for (int j = 0; j < MAXV; ++j) lgs[i][j] += v[i][j];
+    }
+#pragma unroll
+    for (int i = 0; i < RT_TPW; ++i) {
+        const int t = t0 + i;
+        if (t >= T) break;
+        if (logits_out) {
+#pragma unroll
+            for (int j = 0; j < MAXV; ++j) {
+                const int e = lane + j * kWave;
+                if (e < E) logits_out[(size_t)t * E + e] = lgs[i][j];
+            }
+        }
+        route_token<MAXV>(lgs[i], E, K, bias, flags, probs ? probs + (size_t)t * E : nullptr,
                           ids + (size_t)t * K, w + (size_t)t * K, psum, losses, &zacc, csum);
     }
     // Per-block sums over the waves, in wave order (a fixed order).
