@@ -26,11 +26,11 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---- router ----------------------------------------------------------------
 // Number of token blocks of the route kernel (its prob_sum partials are per block).
-int router_num_blocks(int T, int dtype);
+int router_num_blocks(int T, int E);
 // Workspace of the router: W_r^T and partial scores (bf16 scores from x) and
 // the per-block probability sums.
 size_t router_ws_bytes(int T, int d, int E, int dtype);
-// loss_part (optional, router_num_blocks(T) * (E + 1) floats): the route
+// loss_part (optional, router_num_blocks(T, E) * (E + 1) floats): the route
 // kernel's per-block partials of the router regularisers, for
 // launch_router_losses_reduce.
 hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const void* x,

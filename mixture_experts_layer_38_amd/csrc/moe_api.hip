@@ -111,7 +111,7 @@ static ForwardLayout forward_layout(const moe_problem* p) {
                                route_dispatch_small_ws_bytes(p->T, p->n_experts)));
     L.disp_ws = take(dispatch_ws_bytes(p->T, p->top_k, p->n_experts));
     L.ffn_ws = take(ffn_ws_bytes(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype));
-    L.loss_part = take((size_t)router_num_blocks(p->T, p->dtype) * (E + 1) * 4);
+    L.loss_part = take((size_t)router_num_blocks(p->T, p->n_experts) * (E + 1) * 4);
     L.total = o;
     return L;
 }
@@ -186,7 +186,7 @@ static moe_status forward_launch(const moe_problem* p, const ForwardLayout& L, c
                               base + L.disp_ws, s);
         if (err != hipSuccess) return MOE_ERR_HIP;
         if (losses) {
-            err = launch_router_losses_reduce(p->T, p->n_experts, p->top_k, router_num_blocks(p->T, p->dtype),
+            err = launch_router_losses_reduce(p->T, p->n_experts, p->top_k, router_num_blocks(p->T, p->n_experts),
                                               loss_part, counts, D.z_loss, D.aux_topk, s);
             if (err != hipSuccess) return MOE_ERR_HIP;
         }
