@@ -52,7 +52,8 @@ constexpr int PF_SMALL_MIN_E = 32;  // experts from which small groups leave the
 
 int prefill_max_mtiles(int n_rows, int E) { return n_rows / 128 + E + 1; }
 
-// One block; thread e cuts expert e's rows into bm-row tiles: *mt_count
+// One block; zeroes the two GEMMs' tail-claim counters (claim, 2 x 8,
+// optional), and thread e cuts expert e's rows into bm-row tiles: *mt_count
 // row tiles, tile j starting at grouped row mt_row0[j].  mt_expert[j] packs
 // the tile's expert (bits 0-10) and its place in the tile order's groups:
 // each expert's row tiles form ceil(n / PF_GM) groups of balanced sizes, so
@@ -65,12 +66,14 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(int E, int max_mt, int b
                                                        int32_t* __restrict__ mt_expert,
                                                        int32_t* __restrict__ mt_row0,
                                                        int32_t* __restrict__ small_count,
-                                                       int32_t* __restrict__ small_list) {
+                                                       int32_t* __restrict__ small_list,
+                                                       int32_t* __restrict__ claim) {
     __shared__ int wave_tot[1024 / kWave];
     __shared__ int small_tot[1024 / kWave];
     const int e = threadIdx.x;
     const int lane = e & (kWave - 1);
     const int wv = e / kWave;
+    if (claim != nullptr && e < 2 * PF_XCD) claim[e] = 0;  // the GEMMs' tail-claim counters
     const int rows0 = (e < E) ? offsets[e + 1] - offsets[e] : 0;
     // Experts with 1 .. min_rows rows leave the tiled GEMM when they are at
     // least a quarter of all experts (a skewed routing); otherwise every
@@ -136,6 +139,10 @@ __host__ __device__ __forceinline__ PfSplit pf_split(int per_xcd, int cpx) {
     return r;
 }
 constexpr int PF_MAX_CPX = 32;  // compute units per XCD the split buffer is sized for
+// Tail rounds of each XCD's tiles that are claimed at run time, for GEMMs of
+// at least PF_DYN_MIN_ROUNDS rounds per XCD.
+constexpr int PF_DYN_ROUNDS = 2;
+constexpr int PF_DYN_MIN_ROUNDS = 8;
 
 // N: weight rows of one expert (gate/up: F, down: d); K: reduction length,
 // a multiple of PF_BK; n_nt: weight tiles per row tile.  BM: token rows per
@@ -149,7 +156,7 @@ void ffn_prefill_kernel(
     const int32_t* __restrict__ rowmap, int topk, const int32_t* __restrict__ mt_count, const int32_t* __restrict__ mt_expert,
     const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ offsets,
     const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out, int cpx,
-    float* __restrict__ part) {
+    float* __restrict__ part, int32_t* __restrict__ claim, int cus) {
     constexpr int SA = BM * PF_BK;      // bf16 elements of one A stage
     constexpr int SB = PF_BN * PF_BK;   // bf16 elements of one B stage
     constexpr int NTB = BM / 64;        // 32-row token blocks per wave
@@ -173,17 +180,60 @@ void ffn_prefill_kernel(
     const PfSplit sp = GATED ? PfSplit{per_xcd, 0, 1} : pf_split(per_xcd, cpx);
     int kpart = 0;
     constexpr bool split = SPLIT;
+    int t;
     if (SPLIT) {
         const int u = slot;
         if (sp.nsplit <= 1 || u >= sp.rem * sp.nsplit) return;
         slot = sp.full + u / sp.nsplit;
         kpart = u % sp.nsplit;
-    } else if (sp.nsplit > 1 && slot >= sp.full) {
-        return;
+        if (slot >= per_xcd) return;
+        t = xcd * per_xcd + slot;
+        if (t >= tiles) return;
+    } else {
+        // XCD v's main list: its first main(v) tiles (all of them, or those
+        // before the split round).  With claim counters, the last
+        // min(PF_DYN_ROUNDS * cus, main(v)) of them (the tail) are claimed at
+        // run time when the XCDs have at least PF_DYN_MIN_ROUNDS rounds of
+        // tiles each (shorter GEMMs lost more to the claims than they gained
+        // from the balance): the workgroups of slots [main - tail, main + cus) take
+        // the next unclaimed tile of their own XCD's tail, else of another
+        // XCD's (in the order xcd + 1, xcd + 2, ...), so that an XCD that
+        // runs ahead takes over the tail of one that runs behind; the cus
+        // extra workgroups per XCD are the ones that can take over.  Each
+        // tile is still computed whole by one workgroup, so the results do
+        // not depend on which workgroup claims it.
+        auto main_of = [&](int v) {
+            const int nv = min(per_xcd, max(0, tiles - v * per_xcd));
+            return sp.nsplit > 1 ? min(nv, sp.full) : nv;
+        };
+        const int dyn = (claim != nullptr && per_xcd >= PF_DYN_MIN_ROUNDS * cus) ? PF_DYN_ROUNDS * cus : 0;
+        const int mx = main_of(xcd);
+        const int dx = min(dyn, mx);
+        if (slot < mx - dx) {
+            t = xcd * per_xcd + slot;
+        } else {
+            if (dyn == 0 || slot >= mx + cus) return;
+            int* bc = reinterpret_cast<int*>(sA0);  // broadcast through the first LDS slot
+            if (threadIdx.x == 0) {
+                int got = -1;
+                for (int j = 0; j < PF_XCD && got < 0; ++j) {
+                    const int v = (xcd + j) % PF_XCD;
+                    const int mv = main_of(v);
+                    const int dv = min(dyn, mv);
+                    if (dv <= 0) continue;
+                    if (j > 0 && __hip_atomic_load(&claim[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= dv)
+                        continue;
+                    const int i = atomicAdd(&claim[v], 1);
+                    if (i < dv) got = v * per_xcd + (mv - dv) + i;
+                }
+                bc[0] = got;
+            }
+            __syncthreads();
+            t = __builtin_amdgcn_readfirstlane(bc[0]);
+            __syncthreads();  // every wave has read it before the loads refill the slot
+            if (t < 0) return;
+        }
     }
-    if (slot >= per_xcd) return;
-    const int t = xcd * per_xcd + slot;
-    if (t >= tiles) return;
     const PfTile tl = pf_tile(t, n_mt, n_nt, mt_expert, mt_row0, offsets, n_rows);
     const int nt = tl.nt;
     const int e = tl.e;
@@ -832,9 +882,9 @@ static size_t prefill_split_bytes(int n_rows, int E, int d) {
     return align_up(parts * PF_BM_MAX * PF_BN * sizeof(float), 256);
 }
 
-// Plan: [mt_count][mt_expert][mt_row0][small_count][small_list (E)].
+// Plan: [mt_count][mt_expert][mt_row0][small_count][small_list (E)][claim (2 x 8)].
 static size_t prefill_plan_bytes(int n_rows, int E) {
-    return align_up((size_t)(2 + 2 * prefill_max_mtiles(n_rows, E) + E) * sizeof(int32_t), 256);
+    return align_up((size_t)(2 + 2 * prefill_max_mtiles(n_rows, E) + E + 2 * PF_XCD) * sizeof(int32_t), 256);
 }
 
 size_t prefill_ws_bytes(int n_rows, int E, int d) {
@@ -867,27 +917,35 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
                                       const int32_t* mt_count,
                                       const int32_t* mt_expert, const int32_t* mt_row0,
                                       const int32_t* offsets, const bf16* Wa, const bf16* Wb,
-                                      bf16* out, float* part, hipStream_t s) {
+                                      bf16* out, float* part, int32_t* claim, hipStream_t s) {
     const long tiles = (long)max_mt * n_nt;
     if (K % PF_BK == 0) {
+        const int cus = prefill_cpx();  // compute units per XCD (0: unknown)
         // the second GEMM may cut its last round into k ranges (K >= 4 stages)
-        const int cpx = (!GATED && K / PF_BK >= 4) ? prefill_cpx() : 0;
-        const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
+        const int cpx = (!GATED && K / PF_BK >= 4) ? cus : 0;
+        // with claim counters, one more round of workgroups per XCD that can
+        // take over tiles of the others' tails
+        const int xc = claim != nullptr ? cus : 0;
+        const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD + xc) * PF_XCD);
         const unsigned sgrid = (unsigned)(PF_XCD * cpx);  // split units: at most cpx per XCD
         if (bm == 256)
             ffn_prefill_kernel<GATED, 256, 5, false><<<grid, PF_THREADS, 0, s>>>(
-                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
+                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part,
+                claim, xc);
         else
             ffn_prefill_kernel<GATED, 128, 3, false><<<grid, PF_THREADS, 0, s>>>(
-                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
+                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part,
+                claim, xc);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess || cpx == 0 || GATED) return err;
         if (bm == 256)
             ffn_prefill_kernel<false, 256, 5, true><<<sgrid, PF_THREADS, 0, s>>>(
-                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
+                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part,
+                nullptr, 0);
         else
             ffn_prefill_kernel<false, 128, 3, true><<<sgrid, PF_THREADS, 0, s>>>(
-                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part);
+                n_rows, N, K, n_nt, A, rowmap, topk, mt_count, mt_expert, mt_row0, offsets, Wa, Wb, out, cpx, part,
+                nullptr, 0);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         const dim3 rgrid((unsigned)(PF_XCD * (cpx / 2)), (unsigned)(bm / PF_RD_ROWS));
         if (bm == 256)
@@ -927,13 +985,14 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
     int32_t* mt_row0 = mt_expert + max_mt;
     int32_t* small_count = mt_row0 + max_mt;
     int32_t* small_list = small_count + 1;
+    int32_t* claim = small_list + E;  // gate/up counters, then the second GEMM's
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + prefill_plan_bytes(n_rows, E));
     // With many experts some groups are small: those stream their weights
     // through the decode kernel instead of padding a row tile.
     const int small = (E >= PF_SMALL_MIN_E) ? DC_SMALL_ROWS : 0;
     MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_PLAN, s,
                      ffn_plan_kernel<<<1, 1024, 0, s>>>(E, max_mt, bm, small, offsets, mt_count, mt_expert,
-                                                        mt_row0, small_count, small_list));
+                                                        mt_row0, small_count, small_list, claim));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // The timing hook brackets each GEMM step as a whole: the tiled launch,
@@ -941,7 +1000,7 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
     timer_before(MOE_KERNEL_FFN_GATE_UP, s);
     err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, (const bf16*)A,
                                     rowmap, topk, mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
-                                    (const bf16*)w3, (bf16*)act, nullptr, s);
+                                    (const bf16*)w3, (bf16*)act, nullptr, claim, s);
     if (err != hipSuccess) return err;
     if (small) {
         err = launch_small_experts(true, E, n_rows, F, d, A, rowmap, topk, offsets, small_list, small_count, w1,
@@ -952,7 +1011,7 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
     timer_before(MOE_KERNEL_FFN_DOWN, s);
     err = launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
                                      (const bf16*)act, nullptr, 1, mt_count, mt_expert, mt_row0, offsets,
-                                     (const bf16*)w2, nullptr, (bf16*)h, part, s);
+                                     (const bf16*)w2, nullptr, (bf16*)h, part, claim + PF_XCD, s);
     if (err != hipSuccess) return err;
     if (small) {
         err = launch_small_experts(false, E, n_rows, d, F, act, nullptr, 1, offsets, small_list, small_count, w2,
@@ -982,12 +1041,12 @@ hipError_t launch_linear(int n_rows, int N, int K, const void* x, const int32_t*
     int32_t* small_list = small_count + 1;
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + prefill_plan_bytes(n_rows, 1));
     ffn_plan_kernel<<<1, 1024, 0, s>>>(1, max_mt, bm, 0, offs, mt_count, mt_expert, mt_row0, small_count,
-                                       small_list);
+                                       small_list, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     return launch_prefill_gemm<false>(n_rows, N, K, (N + PF_BN - 1) / PF_BN, max_mt, bm, (const bf16*)x, nullptr,
                                       1, mt_count, mt_expert, mt_row0, offs, (const bf16*)w, nullptr, (bf16*)y,
-                                      part, s);
+                                      part, nullptr, s);
 }
 
 }  // namespace moe
