@@ -41,7 +41,15 @@ KERNEL_SOURCES = {
     "decode": ["mixture_experts_layer_38_amd/csrc/kernels/ffn_decode.hip",
                "mixture_experts_layer_38_amd/csrc/device_common.h"],
     "prefill": ["mixture_experts_layer_38_amd/csrc/kernels/ffn_prefill.hip",
+                "mixture_experts_layer_38_amd/csrc/kernels/ffn_tiles.h",
                 "mixture_experts_layer_38_amd/csrc/device_common.h"],
+    # the whole expert FFN of a large batch: the tiled GEMMs and the
+    # small-expert launches (decode kernel file)
+    "ffn": ["mixture_experts_layer_38_amd/csrc/kernels/ffn_prefill.hip",
+            "mixture_experts_layer_38_amd/csrc/kernels/ffn_tiles.h",
+            "mixture_experts_layer_38_amd/csrc/kernels/ffn_decode.hip",
+            "mixture_experts_layer_38_amd/csrc/kernels/ffn.hip",
+            "mixture_experts_layer_38_amd/csrc/device_common.h"],
 }
 
 
@@ -192,14 +200,14 @@ def workload_record(cfg, layer, x, bias, steps: int, warmup: int, use_graph: boo
     """Throughput of one workload with the roofline of its dominant kernel and
     of the whole layer.  The dominant kernel is the gate/up GEMM (kernel
     "ffn_gate_up"), or the whole expert FFN ("ffn": both GEMMs with every
-    launch, the small expert groups on the auxiliary stream included).  The
+    launch, the small-expert launches included).  The
     bound is the MFMA peak when its arithmetic intensity is above the ridge
     point of the two peaks, else HBM."""
     wall, k_ms, counts, kept, spread = time_workload(cfg, layer, x, bias, steps, warmup, kernel, use_graph)
     ms = wall / steps * 1e3
     gb, gf = (ffn_algorithmic if kernel == "ffn" else gate_up_algorithmic)(cfg, kept)
     lb, lf = layer_algorithmic(cfg, kept)
-    family = "decode" if cfg.T <= 64 else "prefill"
+    family = "decode" if cfg.T <= 64 else ("ffn" if kernel == "ffn" else "prefill")
     traffic = load_traffic(cfg.name, kernel, family)
     if gf / gb > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
         ach = gf / (k_ms * 1e-3) / 1e12
@@ -501,8 +509,9 @@ def main():
         "layer": head["layer"],
         "routing": head["routing"],
     }
-    if "variants" in head:
-        result["variants"] = head["variants"]
+    for k in ("variants", "chunked", "chunked_4096"):
+        if k in head:
+            result[k] = head[k]
     for name in ("mixtral_prefill", "dsv3_routed", "capacity_top2"):
         if name in records and name != head_name:
             key = "prefill" if name == "mixtral_prefill" else name

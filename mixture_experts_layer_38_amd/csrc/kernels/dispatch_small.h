@@ -8,7 +8,10 @@
 
 namespace moe {
 
-constexpr int DS_SMALL_MAX = 4096;
+// The single workgroup walks the list in rounds of 64 with one wave (about half
+// a microsecond per round); above this size the three-kernel dispatch is
+// faster (measured at 4096 assignments: 35.8 us here against about 15 us).
+constexpr int DS_SMALL_MAX = 1024;
 
 // Exclusive scan over the 1024 threads of a block (wave scans, then the wave
 // totals in order).  Returns this thread's exclusive prefix; *total gets the sum.

@@ -284,25 +284,29 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
     }
 }
 
-// prob_sum[e] = sum over route blocks of the per-block sums: one wave per
-// expert, lane j takes blocks j, j + 64, ... in double, then a fixed butterfly.
+// prob_sum[e] = sum over route blocks of the per-block sums: one workgroup
+// per expert; thread i adds blocks i, i + 256, ... in block order in double
+// (eight loads in flight), then a fixed pairwise tree over the 256 threads.
 __global__ __launch_bounds__(256) void psum_reduce_kernel(int nblk, int E,
                                                          const float* __restrict__ part,
                                                          float* __restrict__ prob_sum) {
-    const int e = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
-    if (e >= E) return;
-    const int lane = lane_id();
+    __shared__ double red[256];
+    const int e = blockIdx.x;
     double s = 0.0;
-    for (int b0 = lane; b0 < nblk; b0 += 8 * kWave) {  // eight loads in flight, added in block order
+    for (int b0 = threadIdx.x; b0 < nblk; b0 += 8 * 256) {
         float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = b0 + q * kWave < nblk ? part[(size_t)(b0 + q * kWave) * E + e] : 0.0f;
+        for (int q = 0; q < 8; ++q) v[q] = b0 + q * 256 < nblk ? part[(size_t)(b0 + q * 256) * E + e] : 0.0f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) s += (double)v[q];
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) prob_sum[e] = (float)s;
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) prob_sum[e] = (float)red[0];
 }
 
 // ---- scores ---------------------------------------------------------------------
@@ -768,7 +772,7 @@ hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const
     }
     err = launch_route(T, E, K, flags, nsplit, src, logits_out, bias, probs, part, loss_part, ids, w, s);
     if (err != hipSuccess || !prob_sum) return err;
-    psum_reduce_kernel<<<(E + 3) / 4, 256, 0, s>>>(router_num_blocks(T, E), E, part, prob_sum);
+    psum_reduce_kernel<<<E, 256, 0, s>>>(router_num_blocks(T, E), E, part, prob_sum);
     return hipGetLastError();
 }
 
