@@ -338,11 +338,15 @@ __global__ __launch_bounds__(256) void router_transpose_kernel(int d, int E, con
 // out[split][t][e] = sum over d in this split's slice of x[t][k] * W_r^T[e][k].
 // Workgroup tile: 64 tokens (16 per wave) x 16*NEB experts.  The W_r^T rows
 // of each 128-wide chunk of d are shared by the four waves through LDS: they
-// arrive by DMA (global_load_lds) into one of two buffers while the other is
-// multiplied, with chunk c of row r in slot c ^ (r % 16) so that the fragment
-// reads of 16 consecutive rows fall in distinct banks.  Token rows come
-// straight from HBM one chunk ahead.  Lane (r = lane % 16, g = lane / 16); in
-// each 32-wide step both operands take k = 32 s + 8 g + [0, 8).
+// arrive by DMA (global_load_lds) into a ring of three buffers, with chunk c
+// of row r in slot c ^ (r % 16) so that the fragment reads of 16 consecutive
+// rows fall in distinct banks.  Token rows come straight from HBM into a ring
+// of three register sets.  Both streams run two chunks ahead of the MFMAs
+// (the kernel is bound by memory latency: little arithmetic per byte).
+// Every chunk issues the same loads (the ones past the slice at clamped
+// addresses, their values discarded), so one wait count fits every step.
+// Lane (r = lane % 16, g = lane / 16); in each 32-wide step both operands
+// take k = 32 s + 8 g + [0, 8).
 template <int NEB>
 __global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, int kspan,
                                                          const bf16* __restrict__ x,
@@ -351,8 +355,9 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, i
     constexpr int ROWS = 16 * NEB;                // W_r^T rows per workgroup
     constexpr int CH = ROWS * RG_KCH;             // bf16 elements of one chunk
     constexpr int NLD = ROWS * RG_KCH * 2 / 16 / 256;  // 16-byte DMA loads per thread per chunk
+    constexpr int NX = 4;                         // 16-byte token loads per thread per chunk
     static_assert(NLD >= 1, "chunk covers the workgroup");
-    __shared__ __align__(1024) bf16 wb0[CH], wb1[CH];
+    __shared__ __align__(1024) bf16 wb0[CH], wb1[CH], wb2[CH];
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int lane = lane_id();
     const int rl = lane & 15;
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, i
         wcol[i] = ((q % 16) ^ (row & 15)) * 8;
         wsrc[i] = wrt + (size_t)min(eb0 + row, E - 1) * d;
     }
-    auto issue = [&](int c, bf16* dst) {
+    auto issue = [&](int c, bf16* dst) __attribute__((always_inline)) {
         const int kc = k_beg + min(c, max(nch - 1, 0)) * RG_KCH;
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
@@ -383,30 +388,30 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, i
                 (__attribute__((address_space(3))) void*)(dst + (size_t)(wave * kWave + 256 * i) * 8), 16, 0, 0);
     };
     const int kl = g * 8;
-    const bf16* xr = x + (size_t)min(tb * 16 + rl, T - 1) * d + kl;
+    const bf16* xrow = x + (size_t)min(tb * 16 + rl, T - 1) * d;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // raw loads; the values past the slice (or of an idle wave) are zeroed at
+    // their use, so that nothing waits for a load before then
+    auto load_x = [&](int c, u32x4 (&xv)[NX]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < NX; ++s) xv[s] = load16(xrow + min(k_beg + c * RG_KCH + s * 32 + kl, d - 8));
+    };
     f32x4 acc[NEB];
 #pragma unroll
     for (int j = 0; j < NEB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 xc[4], xn[4];
-    issue(0, wb0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int k = k_beg + s * 32;
-        xc[s] = load16_or_zero(xr + k, active && k + kl < k_end);
-    }
-    for (int c = 0; c < nch; ++c) {
-        bf16* cur = (c & 1) ? wb1 : wb0;
-        bf16* nxt = (c & 1) ? wb0 : wb1;
-        // chunk c has landed and every wave is done with chunk c - 1's buffer
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only: this thread's loads of chunk c
-        __syncthreads();
-        issue(c + 1, nxt);
-        const int kn = k_beg + (c + 1) * RG_KCH;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int k = kn + s * 32;
-            xn[s] = load16_or_zero(xr + k, active && c + 1 < nch && k + kl < k_end);
-        }
+    // chunk c of the slice: wait for its W_r^T DMA and token loads (only chunk
+    // c + 1's may still be in flight), make the DMA visible to every wave,
+    // refill the ring slot of chunk c - 1 with chunk c + 2, then multiply.
+    auto step = [&](int c, const bf16* cur, bf16* nxt2, const u32x4 (&xc)[NX], u32x4 (&xn2)[NX])
+        __attribute__((always_inline)) {
+        // (a plain barrier: a fence here would wait for every load in flight;
+        // the ring slot refilled below was last read by the MFMAs of chunk
+        // c - 1, whose fragment reads have completed)
+        __builtin_amdgcn_s_waitcnt(((NLD + NX) & 15) | (7 << 4) | (15 << 8) | ((((NLD + NX) >> 4) & 3) << 14));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(c + 2, nxt2);
+        load_x(c + 2, xn2);
         // W_r^T fragments of step s + 1 are read while step s is multiplied
         bf16x8 wv[2][NEB];
         auto rd = [&](int s, bf16x8 (&f)[NEB]) {
@@ -419,12 +424,26 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, i
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if (s < 3) rd(s + 1, wv[(s + 1) & 1]);
+            const bool ok = active && k_beg + c * RG_KCH + s * 32 + kl < k_end;
+            const u32x4 xs = ok ? xc[s] : zero;
 #pragma unroll
-            for (int j = 0; j < NEB; ++j) acc[j] = mfma16(as_bf16x8(xc[s]), wv[s & 1][j], acc[j]);
+            for (int j = 0; j < NEB; ++j) acc[j] = mfma16(as_bf16x8(xs), wv[s & 1][j], acc[j]);
         }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) xc[s] = xn[s];
+    };
+    u32x4 xa[NX], xb[NX], xc[NX];
+    issue(0, wb0);
+    load_x(0, xa);
+    issue(1, wb1);
+    load_x(1, xb);
+    const int nch3 = nch - nch % 3;
+    for (int c = 0; c < nch3; c += 3) {
+        step(c, wb0, wb2, xa, xc);
+        step(c + 1, wb1, wb0, xb, xa);
+        step(c + 2, wb2, wb1, xc, xb);
     }
+    // the last nch % 3 chunks start again at ring slot 0
+    if (nch3 < nch) step(nch3, wb0, wb2, xa, xc);
+    if (nch3 + 1 < nch) step(nch3 + 1, wb1, wb0, xb, xa);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may outlive the workgroup
     if (!active) return;
     // acc[j][i]: token tb*16 + 4g + i, expert eb0 + 16 j + rl
@@ -441,7 +460,6 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E, i
     }
 }
 
-// fp32 scores: one thread per (token, expert), plain FMA over d.
 // fp32 scores: one wave per (token, expert); lane l takes j = l, l + 64, ...
 // of the token row, then a fixed-order wave sum.
 __global__ __launch_bounds__(256) void router_logits_f32_kernel(int T, int d, int E,
