@@ -414,7 +414,7 @@ def main():
     ap.add_argument("--only", default=None, choices=[None, "mixtral_decode", "mixtral_prefill", "dsv3_routed",
                                                      "capacity_top2"],
                     help="time one workload only (its object becomes the line's headline fields)")
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--other-steps", type=int, default=20, help="steps of the DeepSeek-V3-shaped and capacity layers")
     ap.add_argument("--prefill-chunk", type=int, default=2048)
     ap.add_argument("--no-cpu", action="store_true")
@@ -467,7 +467,7 @@ def main():
             px = to_device(pin["x"], pcfg.dtype)
             pb = torch.from_numpy(pin["logit_bias"]).cuda()
             log("timing mixtral_prefill")
-            rec = workload_record(pcfg, player, px, pb, args.prefill_steps, 2, args.graph, peaks_rec)
+            rec = workload_record(pcfg, player, px, pb, args.prefill_steps, 5, args.graph, peaks_rec)
             rec["chunked"] = time_chunked(pcfg, player, px, pb, args.prefill_chunk, args.prefill_steps)
             rec["chunked_4096"] = time_chunked(pcfg, player, px, pb, 4096, args.prefill_steps)
             if not args.no_variants:
@@ -487,7 +487,7 @@ def main():
         ob = None if oin["logit_bias"] is None else torch.from_numpy(oin["logit_bias"]).cuda()
         del oin
         log(f"timing {name}")
-        records[name] = workload_record(ocfg, olayer, ox, ob, args.other_steps, 3, args.graph, peaks_rec,
+        records[name] = workload_record(ocfg, olayer, ox, ob, args.other_steps, 5, args.graph, peaks_rec,
                                         kernel="ffn")
         del olayer, ox, ob
         torch.cuda.empty_cache()

@@ -5,9 +5,9 @@
 //              routing probability of each token's chosen experts:
 //              f_e = counts[e] / (T K), P'_e = (1/T) sum_t sum_k [ids[t,k] = e] p[t,e],
 //              p = softmax over all E of logits + bias (the routing softmax).
-// Two kernels, no atomics: per-token work writes per-block partial sums (a
-// wave per token, 16 tokens per block, fixed order inside the block), then one
-// block reduces the partials in a fixed order in double.  Inside the layer the
+// No atomics: per-token work writes per-block partial sums (a wave per token,
+// 16 tokens per block, fixed order inside the block), then two small launches
+// reduce the partials in a fixed order in double.  Inside the layer the
 // route kernel writes the same partials from its own softmax (one pass over
 // the scores), and only the reduce kernel runs here.
 #include <math.h>
@@ -22,9 +22,15 @@ constexpr int RL_WAVES = 4;
 
 int router_losses_blocks(int T) { return (T + RL_BT - 1) / RL_BT; }
 
-size_t router_losses_ws_bytes(int T, int E) {
-    return align_up((size_t)router_losses_blocks(T) * (E + 1) * sizeof(float), 256);
+// Second-level partial sums of the reduce: RL_G groups of blocks.
+constexpr int RL_G = 64;
+
+size_t router_losses_part_bytes(int nblk, int E) {
+    return align_up((size_t)nblk * (E + 1) * sizeof(float), 256) +
+           align_up((size_t)RL_G * (E + 1) * sizeof(double), 256);
 }
+
+size_t router_losses_ws_bytes(int T, int E) { return router_losses_part_bytes(router_losses_blocks(T), E); }
 
 // part: [nblk][E] chosen-probability sums, then [nblk] sums of lse^2.
 template <int MAXV>
@@ -92,46 +98,102 @@ __global__ __launch_bounds__(RL_WAVES * kWave) void router_losses_kernel(
     }
 }
 
-// One block of 1024 threads: wave w reduces experts w, w + 16, ... (lanes over
-// blocks, then a fixed butterfly), then thread 0 forms both losses in order.
-__global__ __launch_bounds__(1024) void router_losses_reduce_kernel(
-    int T, int E, int K, int nblk, const float* __restrict__ part, const int32_t* __restrict__ counts,
-    float* __restrict__ z_loss, float* __restrict__ aux_topk) {
-    __shared__ double pe[1024];
-    __shared__ double zs;
-    const int wave = threadIdx.x / kWave;
-    const int lane = lane_id();
-    for (int e = wave; e < E; e += 1024 / kWave) {
+// Reduce of the per-block partials in two launches, in a fixed order and in
+// double.  Level 1: workgroup g of G adds blocks [g nblk / G, (g + 1) nblk / G)
+// in block order for every column (the E experts' chosen-probability sums,
+// then the sum of lse^2), thread c taking columns c, c + 256, ...: consecutive
+// threads read consecutive experts of a block, eight loads in flight.
+__global__ __launch_bounds__(256) void router_losses_reduce1_kernel(int E, int nblk, int G,
+                                                                   const float* __restrict__ part,
+                                                                   double* __restrict__ lvl1) {
+    const int g = blockIdx.x;
+    const int b0 = (int)((long)g * nblk / G), b1 = (int)((long)(g + 1) * nblk / G);
+    for (int c = threadIdx.x; c <= E; c += 256) {
+        // column c of block b: part[b E + c] for an expert, part[nblk E + b] for lse^2
+        const size_t base = c < E ? (size_t)c : (size_t)nblk * E;
+        const size_t stride = c < E ? (size_t)E : 1;
         double s = 0.0;
-        for (int b = lane; b < nblk; b += kWave) s += (double)part[(size_t)b * E + e];
+        for (int b = b0; b < b1; b += 8) {
+            float v[8];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (lane == 0) pe[e] = s;
-    }
-    if (wave == 1024 / kWave - 1) {
-        double s = 0.0;
-        for (int b = lane; b < nblk; b += kWave) s += (double)part[(size_t)nblk * E + b];
+            for (int q = 0; q < 8; ++q) v[q] = b + q < b1 ? part[base + (size_t)(b + q) * stride] : 0.0f;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (lane == 0) zs = s;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        if (z_loss) *z_loss = (float)(zs / (double)T);
-        if (aux_topk) {
-            double acc = 0.0;
-            for (int e = 0; e < E; ++e)
-                acc += (double)counts[e] / ((double)T * K) * (pe[e] / (double)T);
-            *aux_topk = (float)((double)E * acc);
+            for (int q = 0; q < 8; ++q) s += (double)v[q];
         }
+        lvl1[(size_t)g * (E + 1) + c] = s;
     }
 }
 
-hipError_t launch_router_losses_reduce(int T, int E, int K, int nblk, const float* part, const int32_t* counts,
-                                       float* z_loss, float* aux_topk, hipStream_t s) {
-    MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER_LOSSES, s,
-                     router_losses_reduce_kernel<<<1, 1024, 0, s>>>(T, E, K, nblk, part, counts, z_loss, aux_topk));
+// Level 2, one block of 1024 threads: with R threads per expert (the largest
+// power of two with R E <= 1024), thread t adds groups t / E, + R, ... of
+// expert t % E, and a fixed pairwise tree adds each expert's R sums; wave 0
+// adds the G lse^2 sums with a fixed butterfly.  Then the aux terms
+// f_e P'_e go through a fixed pairwise tree, and thread 0 writes both losses.
+__global__ __launch_bounds__(1024) void router_losses_reduce2_kernel(
+    int T, int E, int K, int G, const double* __restrict__ lvl1, const int32_t* __restrict__ counts,
+    float* __restrict__ z_loss, float* __restrict__ aux_topk) {
+    __shared__ double red[1024];
+    __shared__ double zs;
+    const int t = threadIdx.x;
+    const int C = E + 1;
+    int R = 1;
+    while (2 * R * E <= 1024) R *= 2;
+    double s = 0.0;
+    if (t < R * E) {
+        const int e = t % E;
+        for (int g = t / E; g < G; g += 8 * R) {
+            double v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = g + q * R < G ? lvl1[(size_t)(g + q * R) * C + e] : 0.0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s += v[q];
+        }
+    }
+    red[t] = s;
+    if (t < kWave) {
+        double z = t < G ? lvl1[(size_t)t * C + E] : 0.0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+        if (t == 0) zs = z;
+    }
+    __syncthreads();
+    for (int o = R / 2; o > 0; o >>= 1) {
+        if (t < o * E) red[t] += red[t + o * E];
+        __syncthreads();
+    }
+    const double term = t < E ? (double)counts[t] / ((double)T * K) * (red[t] / (double)T) : 0.0;
+    __syncthreads();
+    red[t] = term;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+        if (t < o) red[t] += red[t + o];
+        __syncthreads();
+    }
+    if (t == 0) {
+        if (z_loss) *z_loss = (float)(zs / (double)T);
+        if (aux_topk) *aux_topk = (float)((double)E * red[0]);
+    }
+}
+
+// part: router_losses_part_bytes(nblk, E) bytes, the per-block partials
+// first, the level-1 sums after them.
+static hipError_t reduce_launches(int T, int E, int K, int nblk, float* part, const int32_t* counts,
+                                  float* z_loss, float* aux_topk, hipStream_t s) {
+    const int G = nblk < RL_G ? nblk : RL_G;
+    double* lvl1 = reinterpret_cast<double*>(reinterpret_cast<char*>(part) +
+                                             align_up((size_t)nblk * (E + 1) * sizeof(float), 256));
+    router_losses_reduce1_kernel<<<G, 256, 0, s>>>(E, nblk, G, part, lvl1);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    router_losses_reduce2_kernel<<<1, 1024, 0, s>>>(T, E, K, G, lvl1, counts, z_loss, aux_topk);
     return hipGetLastError();
+}
+
+hipError_t launch_router_losses_reduce(int T, int E, int K, int nblk, float* part, const int32_t* counts,
+                                       float* z_loss, float* aux_topk, hipStream_t s) {
+    hipError_t err = hipSuccess;
+    MOE_TIMED_LAUNCH(MOE_KERNEL_ROUTER_LOSSES, s, err = reduce_launches(T, E, K, nblk, part, counts, z_loss, aux_topk, s));
+    return err;
 }
 
 hipError_t launch_router_losses(int T, int E, int K, const float* logits, const float* bias,
@@ -151,8 +213,7 @@ hipError_t launch_router_losses(int T, int E, int K, const float* logits, const 
                          router_losses_kernel<16><<<nblk, RL_WAVES * kWave, lds, s>>>(T, E, K, logits, bias, ids, part));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    router_losses_reduce_kernel<<<1, 1024, 0, s>>>(T, E, K, nblk, part, counts, z_loss, aux_topk);
-    return hipGetLastError();
+    return reduce_launches(T, E, K, nblk, part, counts, z_loss, aux_topk, s);
 }
 
 }  // namespace moe

@@ -30,8 +30,9 @@ int router_num_blocks(int T, int E);
 // Workspace of the router: W_r^T and partial scores (bf16 scores from x) and
 // the per-block probability sums.
 size_t router_ws_bytes(int T, int d, int E, int dtype);
-// loss_part (optional, router_num_blocks(T, E) * (E + 1) floats): the route
-// kernel's per-block partials of the router regularisers, for
+// loss_part (optional, router_losses_part_bytes(router_num_blocks(T, E), E)
+// bytes): the route kernel's per-block partials of the router regularisers
+// (the first router_num_blocks(T, E) * (E + 1) floats), for
 // launch_router_losses_reduce.
 hipError_t launch_router(int T, int d, int E, int K, int dtype, int flags, const void* x,
                          const void* w_router, const float* bias, float* logits, float* probs,
@@ -75,9 +76,13 @@ hipError_t launch_small_experts(bool gated, int E, int n_rows, int N, int K, con
                                 const int32_t* ecount, const void* wa, const void* wb, void* out, hipStream_t s);
 // ---- router regularisers ----------------------------------------------------
 size_t router_losses_ws_bytes(int T, int E);
-// The final sums of the regularisers from nblk blocks of partials
-// ([nblk][E] chosen-probability sums, then [nblk] squared log-sum-exps).
-hipError_t launch_router_losses_reduce(int T, int E, int K, int nblk, const float* part, const int32_t* counts,
+// Bytes of a partials buffer for nblk blocks: the partials themselves
+// ([nblk][E] chosen-probability sums, then [nblk] squared log-sum-exps), then
+// room for the reduce's second-level sums.
+size_t router_losses_part_bytes(int nblk, int E);
+// The final sums of the regularisers from nblk blocks of partials in part
+// (router_losses_part_bytes(nblk, E) bytes).
+hipError_t launch_router_losses_reduce(int T, int E, int K, int nblk, float* part, const int32_t* counts,
                                        float* z_loss, float* aux_topk, hipStream_t s);
 hipError_t launch_router_losses(int T, int E, int K, const float* logits, const float* bias,
                                 const int32_t* ids, const int32_t* counts, float* z_loss,

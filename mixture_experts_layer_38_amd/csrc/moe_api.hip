@@ -111,7 +111,7 @@ static ForwardLayout forward_layout(const moe_problem* p) {
                                route_dispatch_small_ws_bytes(p->T, p->n_experts)));
     L.disp_ws = take(dispatch_ws_bytes(p->T, p->top_k, p->n_experts));
     L.ffn_ws = take(ffn_ws_bytes(p->T, p->top_k, p->n_experts, p->d_model, p->d_ff, p->dtype));
-    L.loss_part = take((size_t)router_num_blocks(p->T, p->n_experts) * (E + 1) * 4);
+    L.loss_part = take(router_losses_part_bytes(router_num_blocks(p->T, p->n_experts), (int)E));
     L.total = o;
     return L;
 }
