@@ -354,6 +354,39 @@ def time_variants(cfg, layer, x, bias, steps: int, concat: bool = True):
             rec["roofline"] = {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
                                "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
         out["concat_combine"] = rec
+    if cfg.T <= 64:
+        out["skewed_routing"] = time_skewed_decode(cfg, layer, steps)
+    return out
+
+
+def time_skewed_decode(cfg, layer, steps: int):
+    """The decode step on the same weights under a skewed routing: a Zipf(1.2)
+    per-expert logit offset (the prefill batch's skew) at T = 32 and T = 64
+    tokens, with fresh N(0, 1) token rows.  Experts then hold up to 64 rows,
+    which the decode kernels take in passes of 16, 32 or 64 token rows."""
+    import torch
+    from mixture_experts_layer_38_amd.layer import MoELayer
+    from mixture_experts_layer_38_amd.configs import scaled
+    r = np.arange(1, cfg.E + 1, dtype=np.float64)
+    pz = r ** -1.2
+    bias = torch.from_numpy(np.log(pz / pz.sum()).astype(np.float32)).cuda()
+    g = torch.Generator(device="cuda").manual_seed(12)
+    out = {}
+    for T in (32, 64):
+        scfg = scaled(cfg, T=T, skew="zipf", zipf_s=1.2)
+        x = torch.randn(T, cfg.d, device="cuda", generator=g).to(layer.torch_dtype)
+        v = MoELayer(T, cfg.d, cfg.E, cfg.K, cfg.F, cfg.dtype, layer.w_router, layer.w1, layer.w3, layer.w2,
+                     cfg.capacity)
+        y = torch.empty((T, cfg.d), dtype=layer.torch_dtype, device="cuda")
+        dbg = v.alloc_debug()
+        v.forward(x, bias, y=y, dbg=dbg)
+        torch.cuda.synchronize()
+        kept = dbg["kept"].cpu().numpy()
+        ms = _event_ms(lambda: v.forward(x, bias, y=y), steps)
+        lb, _ = layer_algorithmic(scfg, kept)
+        out[f"zipf1.2_t{T}"] = {"ms_per_step": ms, "value": T / (ms * 1e-3), "unit": "tokens/s",
+                                "counts": dbg["counts"].cpu().numpy().tolist(),
+                                "layer_hbm_frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     return out
 
 

@@ -234,16 +234,19 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_kernel(
 // instead of four times.  The two paths are chosen per workgroup; a kernel
 // holding both takes the registers of the larger, so CPI2 is picked to keep
 // that within the single path's occupancy.
-template <bool GATED, int CPI1, int CPI2, bool ALIGNED, int R>
+template <bool GATED, int CPI1, int CPI2, bool ALIGNED, int R, bool FOUR = false>
 __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_expert_kernel(
     int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
     const int32_t* __restrict__ offsets, const bf16* __restrict__ Wa, const bf16* __restrict__ Wb,
     bf16* __restrict__ out) {
     const int e = blockIdx.y;
-    if (min(offsets[e + 1], n_rows) - offsets[e] <= DC_ROWS)
+    const int m = min(offsets[e + 1], n_rows) - offsets[e];
+    if (m <= DC_ROWS)
         ffn_decode_group<GATED, CPI1, 1, ALIGNED, R>(e, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out, K, K);
-    else
+    else if (!FOUR || m <= 2 * DC_ROWS)
         ffn_decode_group<GATED, CPI2, 2, ALIGNED, R>(e, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out, K, K);
+    else
+        ffn_decode_group<GATED, 1, 4, ALIGNED, R>(e, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out, K, K);
 }
 
 // The experts listed in elist[0 .. *ecount) (small groups of a large batch),
@@ -269,16 +272,17 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A
     // bytes in flight per wave: 0.35% faster on the Mixtral-shaped decode
     // batch); the two-block path of experts with more than 16 rows takes one
     // (with two, the kernel's 270 registers would halve its occupancy).
+    // (two is set only on the aligned path, which the launch below assumes)
     bool two = false;
     if constexpr (ALIGNED) two = d % (2 * DC_KCH) == 0;
     if (two)
         MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_GATE_UP, s,
-                         ffn_decode_expert_kernel<true, 2, 1, ALIGNED, 1><<<g1, DC_WAVES * kWave, 0, s>>>(
+                         ffn_decode_expert_kernel<true, 2, 1, true, 1, true><<<g1, DC_WAVES * kWave, 0, s>>>(
                              n_rows, F, d, (const bf16*)A, rowmap, topk, offsets, (const bf16*)w1,
                              (const bf16*)w3, (bf16*)act));
     else
         MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_GATE_UP, s,
-                         ffn_decode_expert_kernel<true, 1, 1, ALIGNED, 1><<<g1, DC_WAVES * kWave, 0, s>>>(
+                         ffn_decode_expert_kernel<true, 1, 1, ALIGNED, 1, true><<<g1, DC_WAVES * kWave, 0, s>>>(
                              n_rows, F, d, (const bf16*)A, rowmap, topk, offsets, (const bf16*)w1,
                              (const bf16*)w3, (bf16*)act));
     hipError_t err = hipGetLastError();
@@ -296,7 +300,7 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A
     if constexpr (ALIGNED) two_f = F % (2 * DC_KCH) == 0;
     if (two_f)
         MOE_TIMED_LAUNCH(MOE_KERNEL_FFN_DOWN, s,
-                         ffn_decode_expert_kernel<false, 2, 2, ALIGNED, 4><<<g2, DC_WAVES * kWave, 0, s>>>(
+                         ffn_decode_expert_kernel<false, 2, 2, true, 4><<<g2, DC_WAVES * kWave, 0, s>>>(
                              n_rows, d, F, (const bf16*)act, nullptr, 1, offsets, (const bf16*)w2, nullptr,
                              (bf16*)h));
     else
