@@ -9,14 +9,15 @@
 //   gemm      : logits as a batched matmul over all tokens (§2.1 of the notes):
 //               each wave owns 16 tokens x 16*NEB experts over one slice of d
 //               and streams its token rows from HBM with 16x16x32 bf16 MFMAs
-//               (the next 128-wide chunk of x is in flight while the current
-//               one is multiplied; W_r^T comes from L2).  Small token counts
-//               split d over the grid so that enough waves stream x; the
-//               per-slice partial scores go to the workspace;
-//   route     : one wave per token sums the slices in slice order (a fixed
-//               order, so the logits are deterministic), adds the bias, and
-//               runs the softmax, the top-K and the renormalisation with lanes
-//               owning experts lane, lane + 64, ...
+//               (two 128-wide chunks of x in flight while the current one is
+//               multiplied; the workgroup's W_r^T rows arrive in LDS by DMA
+//               from L2).  Small token counts split d over the grid so that
+//               enough waves stream x; the per-slice partial scores go to the
+//               workspace;
+//   route     : a wave takes one or two tokens, sums their slices in slice
+//               order (a fixed order, so the logits are deterministic), adds
+//               the bias, and runs the softmax, the top-K and the
+//               renormalisation with lanes owning experts lane, lane + 64, ...
 // fp32 path: a plain FMA kernel for the scores, then the same route kernel.
 #include <math.h>
 
