@@ -33,7 +33,9 @@
 // expert in groups of at most PF_GM row tiles of one expert (row tile fastest
 // inside a group), and XCD x takes the x-th contiguous eighth of that list, so
 // the tiles that run together on one XCD share their token rows and weight
-// rows in its L2.
+// rows in its L2.  In GEMMs of at least 8 rounds per XCD, the last two rounds
+// of each XCD's list are claimed at run time (per-XCD counters), so that an
+// XCD that runs ahead takes over tiles of one that runs behind.
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
