@@ -283,10 +283,11 @@ void ffn_prefill_kernel(
             b_src[j] = Wa + ((size_t)e * N + nr) * K + (size_t)ks0 * PF_BK + c * 8;
         }
     }
-    auto issue_a = [&](int kt, bf16* dA) __attribute__((always_inline)) {
+    // nja: the A loads of a stage (NJA, or NJA / 2 in the half-tile mode)
+    auto issue_a = [&](int kt, bf16* dA, auto nja) __attribute__((always_inline)) {
         const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
-        for (int j = 0; j < NJA; ++j)
+        for (int j = 0; j < decltype(nja)::value; ++j)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[j] + ko),
                                              (__attribute__((address_space(3))) void*)(dA + 8 * (wave + 4 * j) * PF_BK),
                                              16, 0, 0);
@@ -300,12 +301,20 @@ void ffn_prefill_kernel(
                                              16, 0, 0);
     };
     auto issue = [&](int kt, bf16* dA, bf16* dB) __attribute__((always_inline)) {
-        issue_a(kt, dA);
+        issue_a(kt, dA, std::integral_constant<int, NJA>{});
         issue_b(kt, dB);
     };
 
     const int wm = wave & 1;   // token half of the tile (BM / 2 rows)
     const int wn = wave >> 1;  // weight half of the tile (128 rows)
+    // Half-tile mode (256-row tiles holding at most 128 rows): the second
+    // token half holds only padded rows, so instead of two waves owning
+    // 128 x 128 each over the first half and two idle, wave w owns the tile's
+    // weight rows [64 w, 64 w + 64) against its first 128 token rows, and the
+    // second half's token rows are not loaded.  Every wave then multiplies.
+    const bool ht = HALF && (row_end - row0) <= BM / 2;
+    const int wrow0 = ht ? 64 * wave : wn * 128;      // first weight row of the wave's blocks
+    const int trow0 = ht ? 0 : wm * (BM / 2);         // first token row of the wave's blocks
     f32x16 acc[4][NTB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -314,36 +323,37 @@ void ffn_prefill_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-    // Fragment rows: weight rows wn*128 + 32 wb + lane%32, token rows
-    // wm*BM/2 + 32 tb + lane%32; their swizzles are fixed for the whole tile.
+    // Fragment rows: weight rows wrow0 + 32 wb + lane%32, token rows
+    // trow0 + 32 tb + lane%32; their swizzles are fixed for the whole tile.
     const int fhalf = lane >> 5;
     int wsw[4], tsw[NTB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wsw[i] = pf_swz(wn * 128 + i * 32 + (lane & 31));
+    for (int i = 0; i < 4; ++i) wsw[i] = pf_swz(wrow0 + i * 32 + (lane & 31));
 #pragma unroll
-    for (int i = 0; i < NTB; ++i) tsw[i] = pf_swz(wm * (BM / 2) + i * 32 + (lane & 31));
+    for (int i = 0; i < NTB; ++i) tsw[i] = pf_swz(trow0 + i * 32 + (lane & 31));
     struct Frags {
         bf16x8 w[4], t[NTB];
     };
-    // 16-wide k quarter q of a stage: chunk 2q + (lane / 32).  nb: the
-    // token blocks this wave multiplies (NTB, or fewer on a partly filled
-    // tile whose last blocks hold only padded rows).
+    // 16-wide k quarter q of a stage: chunk 2q + (lane / 32).  nb encodes the
+    // wave's blocks: nb < PF_HT, 4 weight blocks x nb token blocks (NTB, or
+    // fewer on a partly filled tile whose last blocks hold only padded rows);
+    // nb = PF_HT + n, the half-tile mode's 2 weight blocks x n token blocks.
     auto read = [&](auto nb, const bf16* cA, const bf16* cB, int q, Frags& f) __attribute__((always_inline)) {
-        constexpr int NB = decltype(nb)::value;
+        constexpr int NB = pf_tblocks(decltype(nb)::value), WB = pf_wblocks(decltype(nb)::value);
         const int c = 2 * q + fhalf;
 #pragma unroll
-        for (int wb = 0; wb < 4; ++wb)
+        for (int wb = 0; wb < WB; ++wb)
             f.w[wb] = *reinterpret_cast<const bf16x8*>(
-                &cB[(wn * 128 + wb * 32 + (lane & 31)) * PF_BK + (c ^ wsw[wb]) * 8]);
+                &cB[(wrow0 + wb * 32 + (lane & 31)) * PF_BK + (c ^ wsw[wb]) * 8]);
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
             f.t[tb] = *reinterpret_cast<const bf16x8*>(
-                &cA[(wm * (BM / 2) + tb * 32 + (lane & 31)) * PF_BK + (c ^ tsw[tb]) * 8]);
+                &cA[(trow0 + tb * 32 + (lane & 31)) * PF_BK + (c ^ tsw[tb]) * 8]);
     };
     auto mma = [&](auto nb, const Frags& f) __attribute__((always_inline)) {
-        constexpr int NB = decltype(nb)::value;
+        constexpr int NB = pf_tblocks(decltype(nb)::value), WB = pf_wblocks(decltype(nb)::value);
 #pragma unroll
-        for (int wb = 0; wb < 4; ++wb)
+        for (int wb = 0; wb < WB; ++wb)
 #pragma unroll
             for (int tb = 0; tb < NB; ++tb) acc[wb][tb] = mfma32(f.w[wb], f.t[tb], acc[wb][tb]);
     };
@@ -353,14 +363,17 @@ void ffn_prefill_kernel(
     // quarter's MFMAs.
     auto interleave = [&](auto nb, auto nv_c) __attribute__((always_inline)) {
         constexpr int NV = decltype(nv_c)::value;
-        constexpr int NM = 4 * decltype(nb)::value;
+        constexpr int NB = pf_tblocks(decltype(nb)::value), WB = pf_wblocks(decltype(nb)::value);
+        constexpr int NM = WB * NB;
         constexpr int DM = NM > 0 ? NM : 1;  // a wave with no blocks has no MFMAs to spread over
-        static_assert(NM == 0 || NV <= NM, "one load per MFMA at most");
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i < 4 + decltype(nb)::value) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (((i + 1) * NV) / DM > (i * NV) / DM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (i < WB + NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            const int nl = ((i + 1) * NV) / DM - (i * NV) / DM;  // loads after MFMA i
+#pragma unroll
+            for (int l = 0; l < (NV + DM - 1) / DM; ++l)
+                if (l < nl) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
     // After the barrier: the last quarter's MFMAs, NV loads and the reads of
@@ -368,7 +381,8 @@ void ffn_prefill_kernel(
     // on a burst of loads with its MFMAs waiting.
     auto interleave_loads = [&](auto nb, auto nv_c) __attribute__((always_inline)) {
         constexpr int NV = decltype(nv_c)::value;
-        constexpr int NM = 4 * decltype(nb)::value, NR = 4 + decltype(nb)::value;
+        constexpr int NB = pf_tblocks(decltype(nb)::value), WB = pf_wblocks(decltype(nb)::value);
+        constexpr int NM = WB * NB, NR = WB + NB;
         constexpr int NI = NM > NV ? NM : NV;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -421,41 +435,58 @@ void ffn_prefill_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
     // pA: the unit that receives A(kt + 2) during this step.
+    //   Half-tile mode: the token rows (half a stage, mostly L2 hits) and the
+    //     weights (a whole stage, streamed from HBM) trade places: the weights
+    //     of stage kt + 2 take the early loads into the "A" unit, the token
+    //     rows the loads after the barrier into the other, so the weights get
+    //     two stages of lead.  The units' roles swap with them (sw below).
     auto step5 = [&](auto nb, int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB, bf16* pA) __attribute__((always_inline)) {
-        constexpr int V0 = (NJA + 2) / 3, V1 = (NJA + 1) / 3, V2 = NJA / 3;
-        static_assert(V0 + V1 + V2 == NJA, "A loads per quarter");
+        constexpr bool SW = pf_wblocks(decltype(nb)::value) == 2;
+        constexpr int NJ = pf_aloads(decltype(nb)::value, NJA);  // A loads of a stage
+        constexpr int NE = SW ? NJB : NJ;  // early loads, spread over the first three quarters
+        constexpr int NL = SW ? NJ : NJB;  // loads after the barrier
+        constexpr int V0 = (NE + 2) / 3, V1 = (NE + 1) / 3, V2 = NE / 3;
+        static_assert(V0 + V1 + V2 == NE, "early loads per quarter");
         const size_t ko = (size_t)min(kt + 2, nk - 1) * PF_BK;
         auto ld = [&](int j) __attribute__((always_inline)) {
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[j] + ko),
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((SW ? b_src[j] : a_src[j]) + ko),
                                              (__attribute__((address_space(3))) void*)(pA + 8 * (wave + 4 * j) * PF_BK),
                                              16, 0, 0);
         };
-        read(nb, cA, cB, 1, fb);
+        // this stage's token rows and weights, and the next stage's
+        const bf16* tA = SW ? cB : cA;
+        const bf16* tB = SW ? cA : cB;
+        const bf16* uA = SW ? nB : nA;
+        const bf16* uB = SW ? nA : nB;
+        read(nb, tA, tB, 1, fb);
 #pragma unroll
         for (int j = 0; j < V0; ++j) ld(j);
         mma(nb, fa);
         interleave(nb, std::integral_constant<int, V0>{});
         __builtin_amdgcn_sched_barrier(0);
-        read(nb, cA, cB, 2, fa);
+        read(nb, tA, tB, 2, fa);
 #pragma unroll
         for (int j = V0; j < V0 + V1; ++j) ld(j);
         mma(nb, fb);
         interleave(nb, std::integral_constant<int, V1>{});
         __builtin_amdgcn_sched_barrier(0);
-        read(nb, cA, cB, 3, fb);
+        read(nb, tA, tB, 3, fb);
 #pragma unroll
-        for (int j = V0 + V1; j < NJA; ++j) ld(j);
+        for (int j = V0 + V1; j < NE; ++j) ld(j);
         mma(nb, fa);
         interleave(nb, std::integral_constant<int, V2>{});
         __builtin_amdgcn_sched_barrier(0);
         PF_WAIT_LGKM0();
-        PF_WAIT_VM(NJA);
+        PF_WAIT_VM(NE);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue_b(kt + 2, cA);
-        read(nb, nA, nB, 0, fa);
+        if constexpr (SW)
+            issue_a(kt + 2, cA, std::integral_constant<int, NJ>{});
+        else
+            issue_b(kt + 2, cA);
+        read(nb, uA, uB, 0, fa);
         mma(nb, fb);
-        interleave_loads(nb, std::integral_constant<int, NJB>{});
+        interleave_loads(nb, std::integral_constant<int, NL>{});
         __builtin_amdgcn_sched_barrier(0);
     };
     // NSLOT 3: stage kt + 2 goes into slot (kt + 2) % 3, freed when stage
@@ -510,19 +541,31 @@ void ffn_prefill_kernel(
     // instance issues the same loads and barriers, so the waves of one
     // workgroup may run different instances.
     auto run = [&](auto nb) __attribute__((always_inline)) {
-        if (HALF) {
+        if constexpr (HALF) {
             bf16* const u0 = sA0;
             bf16* const u1 = sB0;
             bf16* const u2 = sA1;
             bf16* const u3 = sB1;
             bf16* const u4 = sU4;
-            issue_a(0, u0);
-            issue_b(0, u1);
-            issue_a(1, u2);
-            issue_b(1, u3);
-            PF_WAIT_VM(NLD);
+            constexpr int NJ = pf_aloads(decltype(nb)::value, NJA);
+            constexpr bool SW = pf_wblocks(decltype(nb)::value) == 2;  // half-tile mode: roles swapped
+            if constexpr (SW) {
+                issue_b(0, u0);
+                issue_a(0, u1, std::integral_constant<int, NJ>{});
+                issue_b(1, u2);
+                issue_a(1, u3, std::integral_constant<int, NJ>{});
+            } else {
+                issue_a(0, u0, std::integral_constant<int, NJ>{});
+                issue_b(0, u1);
+                issue_a(1, u2, std::integral_constant<int, NJ>{});
+                issue_b(1, u3);
+            }
+            PF_WAIT_VM(NJ + NJB);
             __builtin_amdgcn_s_barrier();
-            read(nb, u0, u1, 0, fa);
+            if constexpr (SW)
+                read(nb, u1, u0, 0, fa);
+            else
+                read(nb, u0, u1, 0, fa);
             const int nk_main = nk - nk % 5;
             for (int k0 = 0; k0 < nk_main; k0 += 5) {
                 step5(nb, k0, u0, u1, u2, u3, u4);
@@ -537,7 +580,7 @@ void ffn_prefill_kernel(
             if (rem > 1) step5(nb, nk_main + 1, u2, u3, u4, u0, u1);
             if (rem > 2) step5(nb, nk_main + 2, u4, u0, u1, u2, u3);
             if (rem > 3) step5(nb, nk_main + 3, u1, u2, u3, u4, u0);
-        } else if (NSLOT == 3) {
+        } else if constexpr (NSLOT == 3) {
             issue(0, sA0, sB0);
             issue(1, sA1, sB1);
             PF_WAIT_VM(NLD);
@@ -572,7 +615,19 @@ void ffn_prefill_kernel(
         using std::integral_constant;
         const int vh = min(max(row_end - row0 - wm * (BM / 2), 0), BM / 2);
         const int nvb = __builtin_amdgcn_readfirstlane((vh + 31) / 32);
-        if (nvb == 0) {
+        const int nhb = __builtin_amdgcn_readfirstlane((row_end - row0 + 31) / 32);  // half-tile mode: 1..4
+        if (ht) {
+            if constexpr (HALF && NTB == 4) {
+                if (nhb == 1)
+                    run(integral_constant<int, PF_HT + 1>{});
+                else if (nhb == 2)
+                    run(integral_constant<int, PF_HT + 2>{});
+                else if (nhb == 3)
+                    run(integral_constant<int, PF_HT + 3>{});
+                else
+                    run(integral_constant<int, PF_HT + 4>{});
+            }
+        } else if (nvb == 0) {
             run(integral_constant<int, 0>{});
         } else if (nvb == 1) {
             run(integral_constant<int, 1>{});
@@ -590,20 +645,23 @@ void ffn_prefill_kernel(
     PF_WAIT_VM(0);
     PF_WAIT_LGKM0();
 
-    // acc[wb][tb][i]: weight row 8*(i/4) + 4*(lane/32) + i%4 of block wb,
-    // token lane % 32 of block tb.
+    // acc[wb][tb][i]: tile weight row wrow0 + 32 wb + 8*(i/4) + 4*(lane/32) +
+    // i%4, tile token row trow0 + 32 tb + lane % 32; the wave holds wbn
+    // weight blocks (4, or 2 in the half-tile mode).
+    const int wbn = ht ? 2 : 4;
     if (SPLIT) {
         // fp32 partial tile [BM][PF_BN], row = token, column = weight row
         float* pt = part + (size_t)((xcd * sp.rem + (slot - sp.full)) * sp.nsplit + kpart) * BM * PF_BN;
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-            float* prow = pt + (size_t)(wm * (BM / 2) + tb * 32 + (lane & 31)) * PF_BN;
+            float* prow = pt + (size_t)(trow0 + tb * 32 + (lane & 31)) * PF_BN;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int wb = 0; wb < 4; ++wb) {
+                    if (wb >= wbn) continue;
                     const f32x16& a = acc[wb][tb];
-                    *reinterpret_cast<f32x4*>(prow + wn * 128 + wb * 32 + 8 * q + 4 * (lane >> 5)) =
+                    *reinterpret_cast<f32x4*>(prow + wrow0 + wb * 32 + 8 * q + 4 * (lane >> 5)) =
                         f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                 }
         }
@@ -611,7 +669,7 @@ void ffn_prefill_kernel(
     }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
-        const int grow = row0 + wm * (BM / 2) + tb * 32 + (lane & 31);
+        const int grow = row0 + trow0 + tb * 32 + (lane & 31);
         if (grow >= row_end) continue;
         bf16* orow = out + (size_t)grow * N;
 #pragma unroll
@@ -620,7 +678,10 @@ void ffn_prefill_kernel(
             if (GATED) {
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
-                    const int f = nt * 128 + wn * 64 + pr * 32 + wr;
+                    if (2 * pr >= wbn) continue;
+                    // the wave's weight rows interleave W1 and W3 in 32-row
+                    // blocks: features nt*128 + wrow0 / 2 + [0, 16 wbn)
+                    const int f = nt * 128 + wrow0 / 2 + pr * 32 + wr;
                     float v[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -636,7 +697,8 @@ void ffn_prefill_kernel(
             } else {
 #pragma unroll
                 for (int wb = 0; wb < 4; ++wb) {
-                    const int c = nt * PF_BN + wn * 128 + wb * 32 + wr;
+                    if (wb >= wbn) continue;
+                    const int c = nt * PF_BN + wrow0 + wb * 32 + wr;
                     const f32x16& a = acc[wb][tb];
                     if (c + 3 < N) {
                         bf16x4 pk = {(bf16)a[4 * q], (bf16)a[4 * q + 1], (bf16)a[4 * q + 2],
