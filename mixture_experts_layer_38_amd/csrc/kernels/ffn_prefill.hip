@@ -283,7 +283,7 @@ void ffn_prefill_kernel(
             b_src[j] = Wa + ((size_t)e * N + nr) * K + (size_t)ks0 * PF_BK + c * 8;
         }
     }
-    // nja: the A loads of a stage (NJA, or NJA / 2 in the half-tile mode)
+    // nja: the A loads of a stage (NJA, or the tile's token blocks in the 1 x 4 layout)
     auto issue_a = [&](int kt, bf16* dA, auto nja) __attribute__((always_inline)) {
         const size_t ko = (size_t)min(kt, nk - 1) * PF_BK;
 #pragma unroll
@@ -307,14 +307,20 @@ void ffn_prefill_kernel(
 
     const int wm = wave & 1;   // token half of the tile (BM / 2 rows)
     const int wn = wave >> 1;  // weight half of the tile (128 rows)
-    // Half-tile mode (256-row tiles holding at most 128 rows): the second
-    // token half holds only padded rows, so instead of two waves owning
-    // 128 x 128 each over the first half and two idle, wave w owns the tile's
-    // weight rows [64 w, 64 w + 64) against its first 128 token rows, and the
-    // second half's token rows are not loaded.  Every wave then multiplies.
-    const bool ht = HALF && (row_end - row0) <= BM / 2;
+    // Token blocks of the tile that hold at least one row of the expert.
+    const int nhb = __builtin_amdgcn_readfirstlane((row_end - row0 + 31) / 32);
+    // 1 x 4 layout (256-row tiles holding at most 224 rows, an expert's last,
+    // partly filled tile): in the 2 x 2 layout the waves of the second token
+    // half would multiply fewer blocks (or none) and wait at every barrier
+    // for those of the first, so instead wave w owns the tile's weight rows
+    // [64 w, 64 w + 64) against all nhb token blocks, and only those blocks'
+    // rows are loaded.  Every wave then multiplies 8 nhb blocks per stage
+    // instead of at most 16.
+    const bool ht = HALF && nhb <= 2 * NTB - 1;
     const int wrow0 = ht ? 64 * wave : wn * 128;      // first weight row of the wave's blocks
     const int trow0 = ht ? 0 : wm * (BM / 2);         // first token row of the wave's blocks
+    // acc[wb + 2 (tb / 4)][tb % 4]: the accumulators of weight block wb and
+    // token block tb (4 x NTB blocks in the 2 x 2 layout, 2 x 2 NTB in 1 x 4).
     f32x16 acc[4][NTB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -326,18 +332,18 @@ void ffn_prefill_kernel(
     // Fragment rows: weight rows wrow0 + 32 wb + lane%32, token rows
     // trow0 + 32 tb + lane%32; their swizzles are fixed for the whole tile.
     const int fhalf = lane >> 5;
-    int wsw[4], tsw[NTB];
+    int wsw[4], tsw[2 * NTB];
 #pragma unroll
     for (int i = 0; i < 4; ++i) wsw[i] = pf_swz(wrow0 + i * 32 + (lane & 31));
 #pragma unroll
-    for (int i = 0; i < NTB; ++i) tsw[i] = pf_swz(trow0 + i * 32 + (lane & 31));
+    for (int i = 0; i < 2 * NTB; ++i) tsw[i] = pf_swz(trow0 + i * 32 + (lane & 31));
     struct Frags {
-        bf16x8 w[4], t[NTB];
+        bf16x8 w[4], t[2 * NTB];
     };
     // 16-wide k quarter q of a stage: chunk 2q + (lane / 32).  nb encodes the
     // wave's blocks: nb < PF_HT, 4 weight blocks x nb token blocks (NTB, or
     // fewer on a partly filled tile whose last blocks hold only padded rows);
-    // nb = PF_HT + n, the half-tile mode's 2 weight blocks x n token blocks.
+    // nb = PF_HT + n, the 1 x 4 layout's 2 weight blocks x n token blocks.
     auto read = [&](auto nb, const bf16* cA, const bf16* cB, int q, Frags& f) __attribute__((always_inline)) {
         constexpr int NB = pf_tblocks(decltype(nb)::value), WB = pf_wblocks(decltype(nb)::value);
         const int c = 2 * q + fhalf;
@@ -355,7 +361,10 @@ void ffn_prefill_kernel(
 #pragma unroll
         for (int wb = 0; wb < WB; ++wb)
 #pragma unroll
-            for (int tb = 0; tb < NB; ++tb) acc[wb][tb] = mfma32(f.w[wb], f.t[tb], acc[wb][tb]);
+            for (int tb = 0; tb < NB; ++tb) {
+                f32x16& a = acc[wb + 2 * (tb >> 2)][tb & 3];
+                a = mfma32(f.w[wb], f.t[tb], a);
+            }
     };
     // Interleave: one MFMA, then one LDS fragment read, for every read of the
     // next quarter, then the remaining MFMAs (the reads issue in the shadow of
@@ -435,11 +444,12 @@ void ffn_prefill_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
     // pA: the unit that receives A(kt + 2) during this step.
-    //   Half-tile mode: the token rows (half a stage, mostly L2 hits) and the
-    //     weights (a whole stage, streamed from HBM) trade places: the weights
-    //     of stage kt + 2 take the early loads into the "A" unit, the token
-    //     rows the loads after the barrier into the other, so the weights get
-    //     two stages of lead.  The units' roles swap with them (sw below).
+    //   1 x 4 layout: the token rows (at most 224 of a stage, mostly L2
+    //     hits) and the weights (a whole stage, streamed from HBM) trade
+    //     places: the weights of stage kt + 2 take the early loads into the
+    //     "A" unit, the token rows the loads after the barrier into the other,
+    //     so the weights get two stages of lead.  The units' roles swap with
+    //     them (SW below).
     auto step5 = [&](auto nb, int kt, bf16* cA, bf16* cB, const bf16* nA, const bf16* nB, bf16* pA) __attribute__((always_inline)) {
         constexpr bool SW = pf_wblocks(decltype(nb)::value) == 2;
         constexpr int NJ = pf_aloads(decltype(nb)::value, NJA);  // A loads of a stage
@@ -548,7 +558,7 @@ void ffn_prefill_kernel(
             bf16* const u3 = sB1;
             bf16* const u4 = sU4;
             constexpr int NJ = pf_aloads(decltype(nb)::value, NJA);
-            constexpr bool SW = pf_wblocks(decltype(nb)::value) == 2;  // half-tile mode: roles swapped
+            constexpr bool SW = pf_wblocks(decltype(nb)::value) == 2;  // 1 x 4 layout: roles swapped
             if constexpr (SW) {
                 issue_b(0, u0);
                 issue_a(0, u1, std::integral_constant<int, NJ>{});
@@ -609,24 +619,33 @@ void ffn_prefill_kernel(
             if (nk - nk_main > 0) step(nb, nk_main, sA0, sB0, sA1, sB1);
         }
     };
-    // Token blocks of this wave that hold at least one row of the expert:
-    // all of them except on the expert's last, partly filled tile.
+    // 1 x 4 layout: the tile's nhb token blocks, 1 .. 7.  2 x 2 layout: the
+    // token blocks of this wave that hold at least one row of the expert
+    // (all of them in the 256-row tiles, which use it only from 225 rows on;
+    // in 128-row tiles, all of them except on an expert's last, partly
+    // filled tile).
     {
         using std::integral_constant;
         const int vh = min(max(row_end - row0 - wm * (BM / 2), 0), BM / 2);
         const int nvb = __builtin_amdgcn_readfirstlane((vh + 31) / 32);
-        const int nhb = __builtin_amdgcn_readfirstlane((row_end - row0 + 31) / 32);  // half-tile mode: 1..4
-        if (ht) {
-            if constexpr (HALF && NTB == 4) {
-                if (nhb == 1)
-                    run(integral_constant<int, PF_HT + 1>{});
-                else if (nhb == 2)
-                    run(integral_constant<int, PF_HT + 2>{});
-                else if (nhb == 3)
-                    run(integral_constant<int, PF_HT + 3>{});
-                else
-                    run(integral_constant<int, PF_HT + 4>{});
-            }
+        if constexpr (HALF) {
+            static_assert(NTB == 4, "the 1 x 4 layout splits a 256-row tile");
+            if (!ht)
+                run(integral_constant<int, NTB>{});
+            else if (nhb == 1)
+                run(integral_constant<int, PF_HT + 1>{});
+            else if (nhb == 2)
+                run(integral_constant<int, PF_HT + 2>{});
+            else if (nhb == 3)
+                run(integral_constant<int, PF_HT + 3>{});
+            else if (nhb == 4)
+                run(integral_constant<int, PF_HT + 4>{});
+            else if (nhb == 5)
+                run(integral_constant<int, PF_HT + 5>{});
+            else if (nhb == 6)
+                run(integral_constant<int, PF_HT + 6>{});
+            else
+                run(integral_constant<int, PF_HT + 7>{});
         } else if (nvb == 0) {
             run(integral_constant<int, 0>{});
         } else if (nvb == 1) {
@@ -645,22 +664,26 @@ void ffn_prefill_kernel(
     PF_WAIT_VM(0);
     PF_WAIT_LGKM0();
 
-    // acc[wb][tb][i]: tile weight row wrow0 + 32 wb + 8*(i/4) + 4*(lane/32) +
-    // i%4, tile token row trow0 + 32 tb + lane % 32; the wave holds wbn
-    // weight blocks (4, or 2 in the half-tile mode).
+    // Block (wb, tb), acc[wb + 2 (tb / 4)][tb % 4], element i: tile weight
+    // row wrow0 + 32 wb + 8*(i/4) + 4*(lane/32) + i%4, tile token row
+    // trow0 + 32 tb + lane % 32; the wave holds wbn weight blocks x tbn token
+    // blocks (4 x NTB, or 2 x 2 NTB in the 1 x 4 layout).
     const int wbn = ht ? 2 : 4;
+    const int tbn = ht ? 2 * NTB : NTB;
+    constexpr int TBMAX = HALF ? 2 * NTB : NTB;  // token blocks of either layout
     if (SPLIT) {
         // fp32 partial tile [BM][PF_BN], row = token, column = weight row
         float* pt = part + (size_t)((xcd * sp.rem + (slot - sp.full)) * sp.nsplit + kpart) * BM * PF_BN;
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
+        for (int tb = 0; tb < TBMAX; ++tb) {
+            if (tb >= tbn) continue;
             float* prow = pt + (size_t)(trow0 + tb * 32 + (lane & 31)) * PF_BN;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int wb = 0; wb < 4; ++wb) {
-                    if (wb >= wbn) continue;
-                    const f32x16& a = acc[wb][tb];
+                    if (wb >= wbn || (tb >= NTB && wb >= 2)) continue;
+                    const f32x16& a = acc[wb + 2 * (tb >> 2)][tb & 3];
                     *reinterpret_cast<f32x4*>(prow + wrow0 + wb * 32 + 8 * q + 4 * (lane >> 5)) =
                         f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                 }
@@ -668,9 +691,9 @@ void ffn_prefill_kernel(
         return;
     }
 #pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) {
+    for (int tb = 0; tb < TBMAX; ++tb) {
         const int grow = row0 + trow0 + tb * 32 + (lane & 31);
-        if (grow >= row_end) continue;
+        if (tb >= tbn || grow >= row_end) continue;
         bf16* orow = out + (size_t)grow * N;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -678,14 +701,15 @@ void ffn_prefill_kernel(
             if (GATED) {
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
-                    if (2 * pr >= wbn) continue;
+                    if (2 * pr >= wbn || (tb >= NTB && pr >= 1)) continue;
                     // the wave's weight rows interleave W1 and W3 in 32-row
                     // blocks: features nt*128 + wrow0 / 2 + [0, 16 wbn)
                     const int f = nt * 128 + wrow0 / 2 + pr * 32 + wr;
                     float v[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        v[r] = silu(acc[2 * pr][tb][4 * q + r]) * acc[2 * pr + 1][tb][4 * q + r];
+                        v[r] = silu(acc[2 * pr + 2 * (tb >> 2)][tb & 3][4 * q + r]) *
+                               acc[2 * pr + 1 + 2 * (tb >> 2)][tb & 3][4 * q + r];
                     if (f + 3 < N) {
                         bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
                         *reinterpret_cast<bf16x4*>(orow + f) = pk;
@@ -697,9 +721,9 @@ void ffn_prefill_kernel(
             } else {
 #pragma unroll
                 for (int wb = 0; wb < 4; ++wb) {
-                    if (wb >= wbn) continue;
+                    if (wb >= wbn || (tb >= NTB && wb >= 2)) continue;
                     const int c = nt * PF_BN + wrow0 + wb * 32 + wr;
-                    const f32x16& a = acc[wb][tb];
+                    const f32x16& a = acc[wb + 2 * (tb >> 2)][tb & 3];
                     if (c + 3 < N) {
                         bf16x4 pk = {(bf16)a[4 * q], (bf16)a[4 * q + 1], (bf16)a[4 * q + 2],
                                      (bf16)a[4 * q + 3]};

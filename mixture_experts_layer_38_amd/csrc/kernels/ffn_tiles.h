@@ -22,12 +22,13 @@ __device__ __forceinline__ int pf_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // The tiled kernel's per-wave block counts, encoded in one compile-time
 // value v: v < PF_HT, 4 weight blocks x v token blocks (32 rows each) per
-// wave; v = PF_HT + n, the half-tile mode's 2 weight blocks x n token blocks,
-// in which a stage loads only the first half of its token rows.
+// wave (the 2 x 2 layout); v = PF_HT + n, the 1 x 4 layout's 2 weight blocks
+// x n token blocks, in which a stage loads only the tile's first n token
+// blocks (load instruction j fills token rows [32 j, 32 j + 32)).
 constexpr int PF_HT = 16;
 __host__ __device__ constexpr int pf_tblocks(int v) { return v >= PF_HT ? v - PF_HT : v; }
 __host__ __device__ constexpr int pf_wblocks(int v) { return v >= PF_HT ? 2 : 4; }
-__host__ __device__ constexpr int pf_aloads(int v, int nja) { return v >= PF_HT ? nja / 2 : nja; }
+__host__ __device__ constexpr int pf_aloads(int v, int nja) { return v >= PF_HT ? v - PF_HT : nja; }
 
 // Tile t of the grouped order: row tile mt (of expert e, rows [row0, row_end))
 // and weight tile nt.  A group of g row tiles starting at row tile m0 owns

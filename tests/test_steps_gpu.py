@@ -138,12 +138,15 @@ def test_ffn_and_combine_steps(orc, name, T, d, F):
 
 
 # Expert group sizes whose last row tile is partly filled at every 32-row
-# boundary: with 256-row tiles (T * K >= 128 E) each wave row of the tile
-# holds 0 to 4 token blocks with rows, with 128-row tiles 0 to 2.  F = 320 also
-# leaves the last weight tile of the first GEMM partly filled, and these small
-# grids run the second GEMM's k-split units.
+# boundary.  With 256-row tiles (T * K >= 128 E) a last tile of 1 to 224 rows
+# (1 to 7 token blocks) runs in the 1 x 4 wave layout, one of 225 to 255 rows
+# in the 2 x 2 layout with 97 to 127 rows in the second token half; with
+# 128-row tiles each wave row of the tile holds 0 to 2 token blocks with rows.
+# F = 320 also leaves the last weight tile of the first GEMM partly filled,
+# and these small grids run the second GEMM's k-split units.
 @pytest.mark.parametrize("name,T,E,sizes", [
     ("tiles256", 1600, 6, [289, 447, 97, 480, 1, 129]),
+    ("tiles256_tails", 1600, 6, [80, 250, 160, 511, 224, 225]),
     ("tiles128", 300, 8, [1, 32, 33, 64, 65, 96, 97, 205]),
 ])
 def test_ffn_partial_tiles(orc, name, T, E, sizes):
