@@ -8,21 +8,25 @@
 // reduction dimension: act = SiLU(X W1^T) * (X W3^T) and h = act W2^T.
 //
 // Tiles.  A device-side plan (one tiny kernel) cuts every expert's rows into
-// 256-row tiles (128-row tiles when the groups average fewer than 128 rows;
-// the same code with half the token blocks).  On an expert's last, partly
-// filled tile each wave runs a copy of the main loop that multiplies only its
-// token blocks holding rows.  An output tile is 256 token rows x 256 weight
-// rows; for gate/up the 256 weight rows are 128 features of W1 and the same
-// 128 of W3, interleaved in 32-row blocks so that the SiLU-gate epilogue stays
-// inside each wave.  Four waves (one per SIMD) split the tile 2 x 2; a wave owns
-// 128 x 128 as 4 x 4 blocks of 32x32 accumulated in AGPRs with
-// v_mfma_f32_32x32x16_bf16 (weights as the first operand, so that each lane
-// ends with four consecutive output columns of one token).
+// 256-row tiles (128-row tiles when the groups average fewer than 128 rows).
+// An output tile is 256 (or 128) token rows x 256 weight rows; for gate/up the
+// 256 weight rows are 128 features of W1 and the same 128 of W3, interleaved
+// in 32-row blocks so that the SiLU-gate epilogue stays inside each wave.
+// Four waves (one per SIMD) split a full tile 2 x 2; a wave owns 128 x 128 as
+// 4 x 4 blocks of 32x32 accumulated in AGPRs with v_mfma_f32_32x32x16_bf16
+// (weights as the first operand, so that each lane ends with four consecutive
+// output columns of one token).  An expert's last, partly filled 256-row tile
+// of at most 224 rows is split 1 x 4 instead: each wave owns 64 weight rows
+// against the tile's token blocks that hold rows (1 to 7), and only those
+// rows are loaded.  In 128-row tiles each wave of a partly filled tile runs a
+// copy of the main loop that multiplies only its token blocks holding rows.
 //
 // Pipeline (K a multiple of 64).  Operand stages are 64 wide in k, so a tile
 // row is one 128-byte line, and go straight from HBM/L2 into LDS with
-// global_load_lds_dwordx4 (no staging registers): two 64 KB slots, the next
-// stage in flight while the current one is multiplied, one barrier per stage.
+// global_load_lds_dwordx4 (no staging registers).  256-row tiles use all
+// 160 KB of the LDS as five 32 KB units that the token and weight halves of
+// consecutive stages take in turn, one half issued two stages ahead, the other
+// one; 128-row tiles use three whole-stage slots.  One barrier per stage.
 // Row r keeps its 16-byte chunk c in slot c ^ swz(r), so the fragment reads
 // of consecutive rows are free of bank conflicts (the global addresses carry
 // the permutation, since the DMA writes lanes in order).  Inside a stage the
