@@ -264,11 +264,17 @@ void ffn_prefill_kernel(
     const int ls = lane & 7;
     const bf16* a_src[NJA];
     const bf16* b_src[NJB];
+    // Token row of A load j.  Through the row map, all its loads go out at
+    // once (a test of the map inside the loop put each behind a wait of its
+    // own), before the weights' first loads, and the rows are formed after
+    // those (src_row's arithmetic).
+    int arow[NJA];
+    if (rowmap != nullptr) {
 #pragma unroll
-    for (int j = 0; j < NJA; ++j) {
-        const int tr = 8 * (wave + 4 * j) + lr;
-        const int r = src_row(rowmap, topk, min(row0 + tr, row_end - 1));
-        a_src[j] = A + (size_t)r * K + (size_t)ks0 * PF_BK + (ls ^ pf_swz(tr)) * 8;
+        for (int j = 0; j < NJA; ++j) arow[j] = rowmap[min(row0 + 8 * (wave + 4 * j) + lr, row_end - 1)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NJA; ++j) arow[j] = min(row0 + 8 * (wave + 4 * j) + lr, row_end - 1);
     }
 #pragma unroll
     for (int j = 0; j < NJB; ++j) {
@@ -323,6 +329,31 @@ void ffn_prefill_kernel(
     const bool ht = HALF && nhb <= 2 * NTB - 1;
     const int wrow0 = ht ? 64 * wave : wn * 128;      // first weight row of the wave's blocks
     const int trow0 = ht ? 0 : wm * (BM / 2);         // first token row of the wave's blocks
+    // Through a row map, the weights of stages 0 and 1 are requested before
+    // the token rows' addresses exist (those wait for the map), into the units
+    // where the main loop expects them; run() then requests the token rows of
+    // both stages.  Loads return in order, so once only the last stage's
+    // token loads are in flight, the map and stage 0 have arrived.  Without a
+    // map, run() requests both stages in the usual order.
+    const bool wfirst = rowmap != nullptr;
+    if (wfirst) {
+        if (HALF && ht) {
+            issue_b(0, sA0);
+            issue_b(1, sA1);
+        } else {
+            issue_b(0, sB0);
+            issue_b(1, sB1);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NJA; ++j) {
+        const int tr = 8 * (wave + 4 * j) + lr;
+        // assignment -> token (src_row): a dropped slot (-1) reads token 0
+        const int a = pf_opaque_v(arow[j]);  // waited for here, after the weights' loads
+        const int r = rowmap != nullptr ? (a < 0 ? 0 : a / topk) : a;
+        a_src[j] = A + (size_t)r * K + (size_t)ks0 * PF_BK + (ls ^ pf_swz(tr)) * 8;
+    }
     // acc[wb + 2 (tb / 4)][tb % 4]: the accumulators of weight block wb and
     // token block tb (4 x NTB blocks in the 2 x 2 layout, 2 x 2 NTB in 1 x 4).
     f32x16 acc[4][NTB];
@@ -563,18 +594,30 @@ void ffn_prefill_kernel(
             bf16* const u4 = sU4;
             constexpr int NJ = pf_aloads(decltype(nb)::value, NJA);
             constexpr bool SW = pf_wblocks(decltype(nb)::value) == 2;  // 1 x 4 layout: roles swapped
-            if constexpr (SW) {
-                issue_b(0, u0);
-                issue_a(0, u1, std::integral_constant<int, NJ>{});
-                issue_b(1, u2);
-                issue_a(1, u3, std::integral_constant<int, NJ>{});
+            // stage s: B in unit 2s + SW, A in unit 2s + 1 - SW
+            if (wfirst) {  // B already requested
+                if constexpr (SW) {
+                    issue_a(0, u1, std::integral_constant<int, NJ>{});
+                    issue_a(1, u3, std::integral_constant<int, NJ>{});
+                } else {
+                    issue_a(0, u0, std::integral_constant<int, NJ>{});
+                    issue_a(1, u2, std::integral_constant<int, NJ>{});
+                }
+                PF_WAIT_VM(NJ);
             } else {
-                issue_a(0, u0, std::integral_constant<int, NJ>{});
-                issue_b(0, u1);
-                issue_a(1, u2, std::integral_constant<int, NJ>{});
-                issue_b(1, u3);
+                if constexpr (SW) {
+                    issue_b(0, u0);
+                    issue_a(0, u1, std::integral_constant<int, NJ>{});
+                    issue_b(1, u2);
+                    issue_a(1, u3, std::integral_constant<int, NJ>{});
+                } else {
+                    issue_a(0, u0, std::integral_constant<int, NJ>{});
+                    issue_b(0, u1);
+                    issue_a(1, u2, std::integral_constant<int, NJ>{});
+                    issue_b(1, u3);
+                }
+                PF_WAIT_VM(NJ + NJB);
             }
-            PF_WAIT_VM(NJ + NJB);
             __builtin_amdgcn_s_barrier();
             if constexpr (SW)
                 read(nb, u1, u0, 0, fa);
@@ -595,9 +638,15 @@ void ffn_prefill_kernel(
             if (rem > 2) step5(nb, nk_main + 2, u4, u0, u1, u2, u3);
             if (rem > 3) step5(nb, nk_main + 3, u1, u2, u3, u4, u0);
         } else if constexpr (NSLOT == 3) {
-            issue(0, sA0, sB0);
-            issue(1, sA1, sB1);
-            PF_WAIT_VM(NLD);
+            if (wfirst) {
+                issue_a(0, sA0, std::integral_constant<int, NJA>{});
+                issue_a(1, sA1, std::integral_constant<int, NJA>{});
+                PF_WAIT_VM(NJA);
+            } else {
+                issue(0, sA0, sB0);
+                issue(1, sA1, sB1);
+                PF_WAIT_VM(NLD);
+            }
             __builtin_amdgcn_s_barrier();
             read(nb, sA0, sB0, 0, fa);
             const int nk_main = nk - nk % 3;
@@ -610,9 +659,15 @@ void ffn_prefill_kernel(
             if (nk - nk_main > 0) step3(nb, nk_main, sA0, sB0, sA1, sB1, sA2, sB2);
             if (nk - nk_main > 1) step3(nb, nk_main + 1, sA1, sB1, sA2, sB2, sA0, sB0);
         } else {
-            issue(0, sA0, sB0);
-            issue(1, sA1, sB1);
-            PF_WAIT_VM(NLD);
+            if (wfirst) {
+                issue_a(0, sA0, std::integral_constant<int, NJA>{});
+                issue_a(1, sA1, std::integral_constant<int, NJA>{});
+                PF_WAIT_VM(NJA);
+            } else {
+                issue(0, sA0, sB0);
+                issue(1, sA1, sB1);
+                PF_WAIT_VM(NLD);
+            }
             __builtin_amdgcn_s_barrier();
             read(nb, sA0, sB0, 0, fa);
             const int nk_main = nk - nk % 2;
@@ -674,6 +729,8 @@ void ffn_prefill_kernel(
     // blocks (4 x NTB, or 2 x 2 NTB in the 1 x 4 layout).
     const int wbn = ht ? 2 : 4;
     const int tbn = ht ? 2 * NTB : NTB;
+    // the lane index again, rather than a value kept across the main loop
+    const int el = pf_opaque_v(lane_id());
     constexpr int TBMAX = HALF ? 2 * NTB : NTB;  // token blocks of either layout
     if (SPLIT) {
         // fp32 partial tile [BM][PF_BN], row = token, column = weight row
@@ -681,14 +738,14 @@ void ffn_prefill_kernel(
 #pragma unroll
         for (int tb = 0; tb < TBMAX; ++tb) {
             if (tb >= tbn) continue;
-            float* prow = pt + (size_t)(trow0 + tb * 32 + (lane & 31)) * PF_BN;
+            float* prow = pt + (size_t)(trow0 + tb * 32 + (el & 31)) * PF_BN;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int wb = 0; wb < 4; ++wb) {
                     if (wb >= wbn || (tb >= NTB && wb >= 2)) continue;
                     const f32x16& a = acc[wb + 2 * (tb >> 2)][tb & 3];
-                    *reinterpret_cast<f32x4*>(prow + wrow0 + wb * 32 + 8 * q + 4 * (lane >> 5)) =
+                    *reinterpret_cast<f32x4*>(prow + wrow0 + wb * 32 + 8 * q + 4 * (el >> 5)) =
                         f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                 }
         }
@@ -696,12 +753,12 @@ void ffn_prefill_kernel(
     }
 #pragma unroll
     for (int tb = 0; tb < TBMAX; ++tb) {
-        const int grow = row0 + trow0 + tb * 32 + (lane & 31);
+        const int grow = row0 + trow0 + tb * 32 + (el & 31);
         if (tb >= tbn || grow >= row_end) continue;
         bf16* orow = out + (size_t)grow * N;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int wr = 8 * q + 4 * (lane >> 5);
+            const int wr = 8 * q + 4 * (el >> 5);
             if (GATED) {
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {

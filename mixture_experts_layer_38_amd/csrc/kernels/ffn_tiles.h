@@ -20,6 +20,16 @@ __device__ __forceinline__ int pf_swz(int r) { return (r ^ (r >> 3)) & 7; }
 // s_waitcnt immediate: lgkmcnt == 0, no wait on the other counters.
 #define PF_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
 
+// v itself, passed through an empty asm statement (no instruction): the
+// compiler keeps it after the memory operations issued before it, so a load
+// whose value goes through it is waited for only here.
+__device__ __forceinline__ int pf_opaque_v(int v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(v));
+#endif
+    return v;
+}
+
 // The tiled kernel's per-wave block counts, encoded in one compile-time
 // value v: v < PF_HT, 4 weight blocks x v token blocks (32 rows each) per
 // wave (the 2 x 2 layout); v = PF_HT + n, the 1 x 4 layout's 2 weight blocks
