@@ -730,7 +730,7 @@ void ffn_prefill_kernel(
     const int wbn = ht ? 2 : 4;
     const int tbn = ht ? 2 * NTB : NTB;
     // the lane index again, rather than a value kept across the main loop
-    const int el = pf_opaque_v(lane_id());
+    const int el = pf_lane_fresh();
     constexpr int TBMAX = HALF ? 2 * NTB : NTB;  // token blocks of either layout
     if (SPLIT) {
         // fp32 partial tile [BM][PF_BN], row = token, column = weight row
@@ -751,51 +751,81 @@ void ffn_prefill_kernel(
         }
         return;
     }
+    // The output through the LDS: each wave puts its block of the tile (token
+    // rows trow0 + [0, 32 TBN), the W bf16 columns of its weight blocks) into
+    // an LDS unit of its own, rows of 2W bytes whose 16-byte chunks are
+    // swizzled by row, then writes whole row segments, 16 bytes per lane and
+    // W / 8 lanes per row (8 B per lane straight from the accumulators would
+    // split every row into 16-byte pieces, one request each).  The barrier
+    // makes sure no wave still reads the ring.
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    auto store_tile = [&](auto wbn_c, auto tbn_c) __attribute__((always_inline)) {
+        constexpr int WBN = decltype(wbn_c)::value, TBN = decltype(tbn_c)::value;
+        constexpr int W = (GATED ? 16 : 32) * WBN;  // bf16 columns of the wave's block
+        constexpr int NCH = W / 8;                   // 16-byte chunks per row
+        constexpr int SWM = NCH < 8 ? NCH - 1 : 7;   // chunk swizzle: chunk ^ (row & SWM)
+        constexpr int RPI = kWave / NCH;             // rows per store instruction
+        // a wave's block fits its unit (the ring's 32 KB units; else the
+        // smallest slot used, an A slot)
+        static_assert(TBN * 32 * W <= (NSLOT == 5 ? SB : SA), "a wave's block fits its LDS unit");
+        bf16* const st = wave == 0 ? (NSLOT == 5 ? sA0 : sB0)
+                       : wave == 1 ? (NSLOT == 5 ? sB0 : sB1)
+                       : wave == 2 ? (NSLOT == 5 ? sA1 : (NSLOT == 3 ? sB2 : sA1))
+                                   : (NSLOT == 5 ? sB1 : sA0);
 #pragma unroll
-    for (int tb = 0; tb < TBMAX; ++tb) {
-        const int grow = row0 + trow0 + tb * 32 + (el & 31);
-        if (tb >= tbn || grow >= row_end) continue;
-        bf16* orow = out + (size_t)grow * N;
+        for (int tb = 0; tb < TBN; ++tb) {
+            if (tb >= tbn) continue;
+            const int rl = tb * 32 + (el & 31);
+            bf16* srow = st + rl * W;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int wr = 8 * q + 4 * (el >> 5);
-            if (GATED) {
+            for (int q = 0; q < 4; ++q) {
+                const int wr = 8 * q + 4 * (el >> 5);
+                if constexpr (GATED) {
 #pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-                    if (2 * pr >= wbn || (tb >= NTB && pr >= 1)) continue;
-                    // the wave's weight rows interleave W1 and W3 in 32-row
-                    // blocks: features nt*128 + wrow0 / 2 + [0, 16 wbn)
-                    const int f = nt * 128 + wrow0 / 2 + pr * 32 + wr;
-                    float v[4];
+                    for (int pr = 0; pr < WBN / 2; ++pr) {
+                        // the wave's weight rows interleave W1 and W3 in
+                        // 32-row blocks: local features pr*32 + wr + [0, 4)
+                        float v[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[r] = silu(acc[2 * pr + 2 * (tb >> 2)][tb & 3][4 * q + r]) *
-                               acc[2 * pr + 1 + 2 * (tb >> 2)][tb & 3][4 * q + r];
-                    if (f + 3 < N) {
-                        bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-                        *reinterpret_cast<bf16x4*>(orow + f) = pk;
-                    } else {
                         for (int r = 0; r < 4; ++r)
-                            if (f + r < N) orow[f + r] = (bf16)v[r];
+                            v[r] = silu(acc[2 * pr + 2 * (tb >> 2)][tb & 3][4 * q + r]) *
+                                   acc[2 * pr + 1 + 2 * (tb >> 2)][tb & 3][4 * q + r];
+                        const int cl = pr * 32 + wr;
+                        *reinterpret_cast<bf16x4*>(srow + (((cl >> 3) ^ (rl & SWM)) << 3) + (cl & 7)) =
+                            bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
                     }
-                }
-            } else {
+                } else {
 #pragma unroll
-                for (int wb = 0; wb < 4; ++wb) {
-                    if (wb >= wbn || (tb >= NTB && wb >= 2)) continue;
-                    const int c = nt * PF_BN + wrow0 + wb * 32 + wr;
-                    const f32x16& a = acc[wb + 2 * (tb >> 2)][tb & 3];
-                    if (c + 3 < N) {
-                        bf16x4 pk = {(bf16)a[4 * q], (bf16)a[4 * q + 1], (bf16)a[4 * q + 2],
-                                     (bf16)a[4 * q + 3]};
-                        *reinterpret_cast<bf16x4*>(orow + c) = pk;
-                    } else {
-                        for (int r = 0; r < 4; ++r)
-                            if (c + r < N) orow[c + r] = (bf16)a[4 * q + r];
+                    for (int wb = 0; wb < WBN; ++wb) {
+                        const f32x16& av = acc[wb + 2 * (tb >> 2)][tb & 3];
+                        const int cl = wb * 32 + wr;
+                        *reinterpret_cast<bf16x4*>(srow + (((cl >> 3) ^ (rl & SWM)) << 3) + (cl & 7)) =
+                            bf16x4{(bf16)av[4 * q], (bf16)av[4 * q + 1], (bf16)av[4 * q + 2], (bf16)av[4 * q + 3]};
                     }
                 }
             }
         }
+        // columns of the wave's block in the output: features nt*128 +
+        // wrow0 / 2 (gate/up), or weight rows nt*256 + wrow0 (N a multiple of 8)
+        const int colbase = GATED ? nt * 128 + wrow0 / 2 : nt * PF_BN + wrow0;
+        const int lrow = el / NCH, lch = el % NCH;
+        const int gcol = colbase + lch * 8;
+#pragma unroll
+        for (int i = 0; i < TBN * 32 / RPI; ++i) {
+            const int rl = i * RPI + lrow;
+            const int grow = row0 + trow0 + rl;
+            const bf16x8 val = *reinterpret_cast<const bf16x8*>(st + rl * W + ((lch ^ (rl & SWM)) << 3));
+            if (grow < row_end && gcol < N) *reinterpret_cast<bf16x8*>(out + (size_t)grow * N + gcol) = val;
+        }
+    };
+    if constexpr (HALF) {
+        if (ht)
+            store_tile(std::integral_constant<int, 2>{}, std::integral_constant<int, 2 * NTB>{});
+        else
+            store_tile(std::integral_constant<int, 4>{}, std::integral_constant<int, NTB>{});
+    } else {
+        store_tile(std::integral_constant<int, 4>{}, std::integral_constant<int, NTB>{});
     }
 }
 
@@ -1060,6 +1090,10 @@ static hipError_t generic_lds_attr() {
     return result[dev];
 }
 
+// Shapes the tiled kernel takes: K a multiple of its 64-wide stages, N a
+// multiple of 8 (its output leaves in 16-byte row chunks).
+static bool pf_tiled_ok(int N, int K) { return K % PF_BK == 0 && N % 8 == 0; }
+
 template <bool GATED>
 static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int max_mt, int bm,
                                       const bf16* A, const int32_t* rowmap, int topk,
@@ -1068,7 +1102,7 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
                                       const int32_t* offsets, const bf16* Wa, const bf16* Wb,
                                       bf16* out, float* part, int32_t* claim, hipStream_t s) {
     const long tiles = (long)max_mt * n_nt;
-    if (K % PF_BK == 0) {
+    if (pf_tiled_ok(N, K)) {
         const int cus = prefill_cpx();  // compute units per XCD (0: unknown)
         // the second GEMM may cut its last round into k ranges (K >= 4 stages)
         const int cpx = (!GATED && K / PF_BK >= 4) ? cus : 0;
@@ -1120,7 +1154,7 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
 // DeepSeek-V3-shaped layer, 128 rows per expert on average: gate/up 3.42 ->
 // 3.28 ms).  The generic variant always uses 256-row tiles.
 static int prefill_bm(int n_rows, int E, int d, int F) {
-    if (d % PF_BK != 0 || F % PF_BK != 0) return 256;
+    if (!pf_tiled_ok(F, d) || !pf_tiled_ok(d, F)) return 256;
     return n_rows >= 128 * E ? 256 : 128;
 }
 
@@ -1182,7 +1216,7 @@ hipError_t launch_linear(int n_rows, int N, int K, const void* x, const int32_t*
                          void* ws, hipStream_t s) {
     if (n_rows <= LIN_SMALL_ROWS) return launch_linear_small(n_rows, N, K, x, offs, w, y, ws, s);
     const int max_mt = prefill_max_mtiles(n_rows, 1);
-    const int bm = (K % PF_BK != 0) ? 256 : (n_rows >= 512 ? 256 : 128);
+    const int bm = !pf_tiled_ok(N, K) ? 256 : (n_rows >= 512 ? 256 : 128);
     int32_t* mt_count = reinterpret_cast<int32_t*>(ws);
     int32_t* mt_expert = mt_count + 1;
     int32_t* mt_row0 = mt_expert + max_mt;

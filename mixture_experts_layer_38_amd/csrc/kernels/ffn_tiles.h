@@ -30,6 +30,16 @@ __device__ __forceinline__ int pf_opaque_v(int v) {
     return v;
 }
 
+// The lane index, computed anew at this point: the compiler cannot reuse an
+// earlier copy (which it would keep in a register across the main loop).
+__device__ __forceinline__ int pf_lane_fresh() {
+    int v = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+#endif
+    return v;
+}
+
 // The tiled kernel's per-wave block counts, encoded in one compile-time
 // value v: v < PF_HT, 4 weight blocks x v token blocks (32 rows each) per
 // wave (the 2 x 2 layout); v = PF_HT + n, the 1 x 4 layout's 2 weight blocks
