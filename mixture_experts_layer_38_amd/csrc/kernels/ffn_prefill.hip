@@ -732,34 +732,56 @@ void ffn_prefill_kernel(
     // the lane index again, rather than a value kept across the main loop
     const int el = pf_lane_fresh();
     constexpr int TBMAX = HALF ? 2 * NTB : NTB;  // token blocks of either layout
-    if (SPLIT) {
-        // fp32 partial tile [BM][PF_BN], row = token, column = weight row
-        float* pt = part + (size_t)((xcd * sp.rem + (slot - sp.full)) * sp.nsplit + kpart) * BM * PF_BN;
-#pragma unroll
-        for (int tb = 0; tb < TBMAX; ++tb) {
-            if (tb >= tbn) continue;
-            float* prow = pt + (size_t)(trow0 + tb * 32 + (el & 31)) * PF_BN;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int wb = 0; wb < 4; ++wb) {
-                    if (wb >= wbn || (tb >= NTB && wb >= 2)) continue;
-                    const f32x16& a = acc[wb + 2 * (tb >> 2)][tb & 3];
-                    *reinterpret_cast<f32x4*>(prow + wrow0 + wb * 32 + 8 * q + 4 * (el >> 5)) =
-                        f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                }
-        }
-        return;
-    }
     // The output through the LDS: each wave puts its block of the tile (token
-    // rows trow0 + [0, 32 TBN), the W bf16 columns of its weight blocks) into
-    // an LDS unit of its own, rows of 2W bytes whose 16-byte chunks are
-    // swizzled by row, then writes whole row segments, 16 bytes per lane and
-    // W / 8 lanes per row (8 B per lane straight from the accumulators would
-    // split every row into 16-byte pieces, one request each).  The barrier
-    // makes sure no wave still reads the ring.
+    // rows trow0 + [0, 32 TBN), the W columns of its weight blocks) into an
+    // LDS unit of its own, rows whose 16-byte chunks are swizzled by row, then
+    // writes whole row segments, 16 bytes per lane (16 bytes per lane straight
+    // from the accumulators would split every row into 16-byte pieces, one
+    // request each, 32 rows per instruction).  The barrier makes sure no wave
+    // still reads the ring.
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    bf16* const st = wave == 0 ? (NSLOT == 5 ? sA0 : sB0)
+                   : wave == 1 ? (NSLOT == 5 ? sB0 : sB1)
+                   : wave == 2 ? (NSLOT == 5 ? sA1 : (NSLOT == 3 ? sB2 : sA1))
+                               : (NSLOT == 5 ? sB1 : sA0);
+    constexpr int UNIT = (NSLOT == 5 ? SB : SA) * (int)sizeof(bf16);  // bytes of the smallest unit used
+    // SPLIT: the fp32 partial tile [BM][PF_BN] (row = token, column = weight
+    // row) of this k range, in passes of rows that fit the unit.
+    auto store_part = [&](auto wbn_c, auto tbn_c) __attribute__((always_inline)) {
+        constexpr int WBN = decltype(wbn_c)::value, TBN = decltype(tbn_c)::value;
+        constexpr int W = 32 * WBN;                 // fp32 columns of the wave's block
+        constexpr int NCH = W / 4;                  // 16-byte chunks per row
+        constexpr int RP = UNIT / (W * 4);          // rows per pass
+        constexpr int RPI = kWave / NCH;            // rows per store instruction
+        static_assert(RP % 32 == 0 && (TBN * 32) % RP == 0, "whole token blocks per pass");
+        float* const sf = reinterpret_cast<float*>(st);
+        float* pt = part + (size_t)((xcd * sp.rem + (slot - sp.full)) * sp.nsplit + kpart) * BM * PF_BN;
+#pragma unroll
+        for (int pass = 0; pass < TBN * 32 / RP; ++pass) {
+#pragma unroll
+            for (int tb = pass * RP / 32; tb < (pass + 1) * RP / 32; ++tb) {
+                if (tb >= tbn) continue;
+                const int rl = tb * 32 + (el & 31) - pass * RP;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int wb = 0; wb < WBN; ++wb) {
+                        const f32x16& a = acc[wb + 2 * (tb >> 2)][tb & 3];
+                        const int cl = wb * 32 + 8 * q + 4 * (el >> 5);
+                        *reinterpret_cast<f32x4*>(sf + rl * W + (((cl >> 2) ^ (rl & 7)) << 2)) =
+                            f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                    }
+            }
+            const int lrow = el / NCH, lch = el % NCH;
+#pragma unroll
+            for (int i = 0; i < RP / RPI; ++i) {
+                const int rl = i * RPI + lrow;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(sf + rl * W + ((lch ^ (rl & 7)) << 2));
+                *reinterpret_cast<f32x4*>(pt + (size_t)(trow0 + pass * RP + rl) * PF_BN + wrow0 + lch * 4) = v;
+            }
+        }
+    };
     auto store_tile = [&](auto wbn_c, auto tbn_c) __attribute__((always_inline)) {
         constexpr int WBN = decltype(wbn_c)::value, TBN = decltype(tbn_c)::value;
         constexpr int W = (GATED ? 16 : 32) * WBN;  // bf16 columns of the wave's block
@@ -768,11 +790,7 @@ void ffn_prefill_kernel(
         constexpr int RPI = kWave / NCH;             // rows per store instruction
         // a wave's block fits its unit (the ring's 32 KB units; else the
         // smallest slot used, an A slot)
-        static_assert(TBN * 32 * W <= (NSLOT == 5 ? SB : SA), "a wave's block fits its LDS unit");
-        bf16* const st = wave == 0 ? (NSLOT == 5 ? sA0 : sB0)
-                       : wave == 1 ? (NSLOT == 5 ? sB0 : sB1)
-                       : wave == 2 ? (NSLOT == 5 ? sA1 : (NSLOT == 3 ? sB2 : sA1))
-                                   : (NSLOT == 5 ? sB1 : sA0);
+        static_assert(TBN * 32 * W * (int)sizeof(bf16) <= UNIT, "a wave's block fits its LDS unit");
 #pragma unroll
         for (int tb = 0; tb < TBN; ++tb) {
             if (tb >= tbn) continue;
@@ -819,13 +837,19 @@ void ffn_prefill_kernel(
             if (grow < row_end && gcol < N) *reinterpret_cast<bf16x8*>(out + (size_t)grow * N + gcol) = val;
         }
     };
+    auto store = [&](auto wbn_c, auto tbn_c) __attribute__((always_inline)) {
+        if constexpr (SPLIT)
+            store_part(wbn_c, tbn_c);
+        else
+            store_tile(wbn_c, tbn_c);
+    };
     if constexpr (HALF) {
         if (ht)
-            store_tile(std::integral_constant<int, 2>{}, std::integral_constant<int, 2 * NTB>{});
+            store(std::integral_constant<int, 2>{}, std::integral_constant<int, 2 * NTB>{});
         else
-            store_tile(std::integral_constant<int, 4>{}, std::integral_constant<int, NTB>{});
+            store(std::integral_constant<int, 4>{}, std::integral_constant<int, NTB>{});
     } else {
-        store_tile(std::integral_constant<int, 4>{}, std::integral_constant<int, NTB>{});
+        store(std::integral_constant<int, 4>{}, std::integral_constant<int, NTB>{});
     }
 }
 
