@@ -250,16 +250,25 @@ __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_decode_expert_kernel(
 }
 
 // The experts listed in elist[0 .. *ecount) (small groups of a large batch),
-// taken in turn by the gridDim.y workgroups of each strip.
-template <bool GATED, int CPI, int NCB, bool ALIGNED, int R>
+// taken in turn by the gridDim.y workgroups of each strip; like the decode
+// kernel, an expert of at most 16 rows runs in passes of one token block
+// (CPI1 chunks per iteration), a larger one in passes of two (CPI2).
+template <bool GATED, int CPI1, int CPI2, bool ALIGNED, int R>
 __global__ __launch_bounds__(DC_WAVES * kWave) void ffn_small_experts_kernel(
     int n_rows, int N, int K, const bf16* __restrict__ A, const int32_t* __restrict__ rowmap, int topk,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ elist, const int32_t* __restrict__ ecount,
     const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, bf16* __restrict__ out) {
     const int cnt = *ecount;
-    for (int i = blockIdx.y; i < cnt; i += gridDim.y)
-        ffn_decode_group<GATED, CPI, NCB, ALIGNED, R>(elist[i], n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb,
-                                                      out, K, K);
+    for (int i = blockIdx.y; i < cnt; i += gridDim.y) {
+        const int e = elist[i];
+        const int m = min(offsets[e + 1], n_rows) - offsets[e];
+        if (m <= DC_ROWS)
+            ffn_decode_group<GATED, CPI1, 1, ALIGNED, R>(e, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out, K,
+                                                         K);
+        else
+            ffn_decode_group<GATED, CPI2, 2, ALIGNED, R>(e, n_rows, N, K, A, rowmap, topk, offsets, Wa, Wb, out, K,
+                                                         K);
+    }
 }
 
 template <bool ALIGNED>
@@ -312,23 +321,37 @@ static hipError_t launch_decode_t(int n_rows, int E, int d, int F, const void* A
 }
 
 // Experts with at most DC_SMALL_ROWS rows inside a larger batch (listed by the
-// tile plan): one pass of 32 token rows over each weight row, so every weight
-// byte is read once; gy = min(E, 64) workgroups per strip take the experts in turn.
+// tile plan): one pass of 16 or 32 token rows over each weight row, so every
+// weight byte is read once; gy = min(E, 64) workgroups per strip take the
+// experts in turn.
 template <bool ALIGNED>
 static hipError_t launch_small_experts_t(bool gated, int gy, int n_rows, int N, int K, const void* A,
                                          const int32_t* rowmap, int topk, const int32_t* offsets,
                                          const int32_t* elist, const int32_t* ecount, const void* wa,
                                          const void* wb, void* out, hipStream_t s) {
+    // two 128-wide chunks per iteration on the one-block path when they tile K
+    bool two = false;
+    if constexpr (ALIGNED) two = K % (2 * DC_KCH) == 0;
     if (gated) {
         dim3 g((N + DC_ROWS - 1) / DC_ROWS, gy);
-        ffn_small_experts_kernel<true, 1, 2, ALIGNED, 1><<<g, DC_WAVES * kWave, 0, s>>>(
-            n_rows, N, K, (const bf16*)A, rowmap, topk, offsets, elist, ecount, (const bf16*)wa, (const bf16*)wb,
-            (bf16*)out);
+        if (two)
+            ffn_small_experts_kernel<true, 2, 1, true, 1><<<g, DC_WAVES * kWave, 0, s>>>(
+                n_rows, N, K, (const bf16*)A, rowmap, topk, offsets, elist, ecount, (const bf16*)wa,
+                (const bf16*)wb, (bf16*)out);
+        else
+            ffn_small_experts_kernel<true, 1, 1, ALIGNED, 1><<<g, DC_WAVES * kWave, 0, s>>>(
+                n_rows, N, K, (const bf16*)A, rowmap, topk, offsets, elist, ecount, (const bf16*)wa,
+                (const bf16*)wb, (bf16*)out);
     } else {
         dim3 g((N + 2 * DC_ROWS - 1) / (2 * DC_ROWS), gy);
-        ffn_small_experts_kernel<false, 1, 2, ALIGNED, 2><<<g, DC_WAVES * kWave, 0, s>>>(
-            n_rows, N, K, (const bf16*)A, nullptr, 1, offsets, elist, ecount, (const bf16*)wa, nullptr,
-            (bf16*)out);
+        if (two)
+            ffn_small_experts_kernel<false, 2, 1, true, 2><<<g, DC_WAVES * kWave, 0, s>>>(
+                n_rows, N, K, (const bf16*)A, nullptr, 1, offsets, elist, ecount, (const bf16*)wa, nullptr,
+                (bf16*)out);
+        else
+            ffn_small_experts_kernel<false, 1, 1, ALIGNED, 2><<<g, DC_WAVES * kWave, 0, s>>>(
+                n_rows, N, K, (const bf16*)A, nullptr, 1, offsets, elist, ecount, (const bf16*)wa, nullptr,
+                (bf16*)out);
     }
     return hipGetLastError();
 }
