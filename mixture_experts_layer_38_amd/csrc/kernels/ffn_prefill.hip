@@ -1119,13 +1119,20 @@ static hipError_t generic_lds_attr() {
 static bool pf_tiled_ok(int N, int K) { return K % PF_BK == 0 && N % 8 == 0; }
 
 template <bool GATED>
-static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int max_mt, int bm,
+static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int max_mt, int bm, int E,
                                       const bf16* A, const int32_t* rowmap, int topk,
                                       const int32_t* mt_count,
                                       const int32_t* mt_expert, const int32_t* mt_row0,
                                       const int32_t* offsets, const bf16* Wa, const bf16* Wb,
                                       bf16* out, float* part, int32_t* claim, hipStream_t s) {
-    const long tiles = (long)max_mt * n_nt;
+    // Workgroups for the plan's row tiles: the groups hold at most n_rows rows
+    // (offsets is a prefix sum ending at or below n_rows), so there are at
+    // most n_rows / bm full tiles plus one partly filled tile per expert.
+    // The grid follows that bound rather than max_mt (sized for 128-row
+    // tiles), since every workgroup past the real tiles is still dispatched,
+    // at the end of the launch, only to exit.
+    const long mts = std::min((long)max_mt, (long)n_rows / bm + E + 1);
+    const long tiles = mts * n_nt;
     if (pf_tiled_ok(N, K)) {
         const int cus = prefill_cpx();  // compute units per XCD (0: unknown)
         // the second GEMM may cut its last round into k ranges (K >= 4 stages)
@@ -1163,7 +1170,7 @@ static hipError_t launch_prefill_gemm(int n_rows, int N, int K, int n_nt, int ma
                                                                offsets, part, out);
         return hipGetLastError();
     }
-    const unsigned grid = (unsigned)(((tiles + PF_XCD - 1) / PF_XCD) * PF_XCD);
+    const unsigned grid = (unsigned)((((long)max_mt * n_nt + PF_XCD - 1) / PF_XCD) * PF_XCD);
     hipError_t aerr = generic_lds_attr<GATED>();
     if (aerr != hipSuccess) return aerr;
     ffn_prefill_generic_kernel<GATED><<<grid, PG_THREADS, PG_LDS_BYTES, s>>>(
@@ -1205,7 +1212,7 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
     // The timing hook brackets each GEMM step as a whole: the tiled launch,
     // the small-expert launch and (second GEMM) the k-split launches.
     timer_before(MOE_KERNEL_FFN_GATE_UP, s);
-    err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, (const bf16*)A,
+    err = launch_prefill_gemm<true>(n_rows, F, d, (F + 127) / 128, max_mt, bm, E, (const bf16*)A,
                                     rowmap, topk, mt_count, mt_expert, mt_row0, offsets, (const bf16*)w1,
                                     (const bf16*)w3, (bf16*)act, nullptr, claim, s);
     if (err != hipSuccess) return err;
@@ -1216,7 +1223,7 @@ hipError_t launch_ffn_prefill(int n_rows, int E, int d, int F, const void* A, co
     }
     timer_after(MOE_KERNEL_FFN_GATE_UP, s);
     timer_before(MOE_KERNEL_FFN_DOWN, s);
-    err = launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm,
+    err = launch_prefill_gemm<false>(n_rows, d, F, (d + PF_BN - 1) / PF_BN, max_mt, bm, E,
                                      (const bf16*)act, nullptr, 1, mt_count, mt_expert, mt_row0, offsets,
                                      (const bf16*)w2, nullptr, (bf16*)h, part, claim + PF_XCD, s);
     if (err != hipSuccess) return err;
@@ -1251,7 +1258,7 @@ hipError_t launch_linear(int n_rows, int N, int K, const void* x, const int32_t*
                                        small_list, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_prefill_gemm<false>(n_rows, N, K, (N + PF_BN - 1) / PF_BN, max_mt, bm, (const bf16*)x, nullptr,
+    return launch_prefill_gemm<false>(n_rows, N, K, (N + PF_BN - 1) / PF_BN, max_mt, bm, 1, (const bf16*)x, nullptr,
                                       1, mt_count, mt_expert, mt_row0, offs, (const bf16*)w, nullptr, (bf16*)y,
                                       part, nullptr, s);
 }
