@@ -147,6 +147,9 @@ def test_ffn_and_combine_steps(orc, name, T, d, F):
 @pytest.mark.parametrize("name,T,E,sizes", [
     ("tiles256", 1600, 6, [289, 447, 97, 480, 1, 129]),
     ("tiles256_tails", 1600, 6, [80, 250, 160, 511, 224, 225]),
+    # every group one row past a whole tile and all T * K rows kept: 12 row
+    # tiles against the launch's bound of T * K / 256 + E + 1 = 13
+    ("tiles256_bound", 771, 6, [257] * 6),
     ("tiles128", 300, 8, [1, 32, 33, 64, 65, 96, 97, 205]),
 ])
 def test_ffn_partial_tiles(orc, name, T, E, sizes):
